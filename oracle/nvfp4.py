@@ -1,0 +1,94 @@
+"""NVFP4 quantization and dequantization.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+Definition followed:
+
+* loopquant page, section 0.2: E2M1 elements, 16-element blocks, one E4M3
+  block scale per block, one FP32 tensor scale; the decoded value of an
+  element is code value x block scale x tensor scale.
+* loopquant page, section 2.2 (paragraph applying the residue bound to the
+  signed E2M1 code book): default tensor scale s_tensor = max|W| / (6*256);
+  the candidate E4M3 block scale is rounded UP, which guarantees that the
+  normalised value |x / s| is at most 6.
+* "Why Gated DeltaNet Survives 4-Bit Quantization", background box "NVFP4
+  and W4A4": the block scale is the block maximum / 6 (before the tensor
+  scale is divided out); block max/RMS is at most 4 in a 16-element block.
+
+The order of the fp32 operations is the reading this project takes where the
+pages are silent (recorded in the design notes): every step is a single
+IEEE binary32 operation with round-to-nearest-even.
+
+    A    = max |x| over the tensor                    (or a given s_t)
+    s_t  = fl(A / 1536)                                 (0 if A == 0)
+    a_b  = max |x_i| over the block
+    s_b  = ceil_E4M3( fl(a_b / fl(6 * s_t)) )           (0 if a_b == 0 or s_t == 0)
+    s    = fl(s_t * s_b);  rho = fl(1 / s)
+    v_i  = fl(x_i * rho);  code_i = nearest E2M1 code of v_i
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import e2m1_round, e2m1_decode, e4m3_ceil, e4m3_decode
+
+BLOCK = 16
+F32 = np.float32
+
+
+def tensor_scale_from_amax(amax) -> np.float32:
+    """s_t = fl(A / (6*256)) in binary32 (loopquant page, section 2.2)."""
+    a = F32(amax)
+    return F32(a / F32(1536.0))
+
+
+def block_scales(x: np.ndarray, s_t) -> np.ndarray:
+    """E4M3 block-scale bytes for a float32 [R, K] tensor (K % 16 == 0)."""
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    assert K % BLOCK == 0
+    s_t = F32(s_t)
+    a_b = np.abs(x).reshape(R, K // BLOCK, BLOCK).max(axis=-1)       # exact
+    six_st = F32(F32(6.0) * s_t)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (a_b / six_st).astype(F32)                                # fl32 division
+    y = np.where((a_b == 0) | (s_t == 0), F32(0), y)
+    return e4m3_ceil(y.astype(np.float64))
+
+
+def quantize(x: np.ndarray, tensor_scale=None):
+    """NVFP4-quantize a float32 [R, K] tensor.
+
+    Returns ``(codes, scales, s_t)``: ``codes`` uint8 [R, K] (one 4-bit code
+    per element, unpacked), ``scales`` uint8 [R, K/16] (E4M3 bytes),
+    ``s_t`` float32.  With ``tensor_scale`` given it is used as s_t.
+    """
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    if tensor_scale is None:
+        s_t = tensor_scale_from_amax(np.abs(x).max() if x.size else F32(0))
+    else:
+        s_t = F32(tensor_scale)
+    sb_bytes = block_scales(x, s_t)
+    s_b = e4m3_decode(sb_bytes).astype(F32)                      # exact in fp32
+    s = (s_t * s_b).astype(F32)                                  # fl32 product
+    with np.errstate(divide="ignore"):
+        rho = (F32(1.0) / s).astype(F32)                         # fl32 reciprocal
+    rho_e = np.repeat(rho, BLOCK, axis=1)
+    with np.errstate(invalid="ignore"):                          # 0 * inf in zero blocks
+        v = (x * rho_e).astype(F32)
+    codes = np.empty((R, K), dtype=np.uint8)
+    for r0 in range(0, R, 256):                                  # chunk to bound memory
+        codes[r0:r0 + 256] = e2m1_round(v[r0:r0 + 256])
+    zero_blk = np.repeat(s == 0, BLOCK, axis=1)
+    codes[zero_blk] = 0
+    return codes, sb_bytes, s_t
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, s_t) -> np.ndarray:
+    """Exact float64 value of every element: value(code) * s_b * s_t
+    (at most 2 + 4 + 24 significant bits, so float64 holds it exactly)."""
+    q = e2m1_decode(codes)
+    sb = np.repeat(e4m3_decode(scales), BLOCK, axis=1)
+    return q * sb * np.float64(F32(s_t))

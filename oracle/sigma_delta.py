@@ -1,0 +1,115 @@
+"""First-order Sigma-Delta weight re-quantization across loop steps.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+Definition (loopquant page, section 2.1 "First-order Sigma-Delta", section
+2.2 "Conservative residue bound on the non-uniform NVFP4 code book" and the
+STE listing of section 2.5): with a FIXED scale and r_0 = 0, at each access
+k = 1..R
+
+    v_k = x + r_{k-1};   q_k = Q(v_k);   r_k = v_k - q_k
+
+where Q is the nearest-point quantizer of a finite code book that saturates
+to its end points.  Section 2.1 shows E_k = r_{k-1} - r_k, so the errors
+telescope: sum_{k<=m} (q_k - x) = -r_m.  Section 2.2 proves |r_k| <= d/2 when
+x lies in the hull [c_0, c_N] of the code book (d = largest neighbour gap),
+and shows that C = {0, 1}, x = 2 diverges.  For E2M1, d = 2, so |r_k| <= 1 in
+normalised units.  The listing zeroes r at the start of every forward and
+normalises x = W / s with a block scale fixed for that forward.
+
+Two forms are provided:
+
+* :func:`sigma_delta_exact` -- the recurrence on an arbitrary finite code
+  book in exact rational arithmetic (``fractions.Fraction``), with a
+  pluggable rounding rule; used for the worked example and the bound tests;
+* :func:`sigma_delta_nvfp4` -- the NVFP4 form the hot path computes, in
+  binary32: the fixed scale is the NVFP4 recipe of ``oracle.nvfp4`` computed
+  once from the fp32 master W; x = clamp(fl(W * rho), -6, 6) (the clamp is
+  the "x inside the hull" hypothesis of section 2.2; it only moves values
+  that fl rounding pushed a few ulp past 6); v = fl(x + r); q = nearest E2M1
+  code; r = v - value(q), which is exact in binary32 and is checked to be.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+from typing import Callable, List, Sequence, Tuple
+
+import numpy as np
+
+from .formats import e2m1_round, e2m1_decode, e4m3_decode
+from . import nvfp4
+
+F32 = np.float32
+
+
+def nearest_saturating(codebook: Sequence[Fraction]) -> Callable[[Fraction], Fraction]:
+    """Nearest-point quantizer of a finite sorted code book that saturates to
+    the end points (ties go to the lower point; the worked example below
+    uses its own rounding rule)."""
+    cb = sorted(Fraction(c) for c in codebook)
+
+    def q(v: Fraction) -> Fraction:
+        if v <= cb[0]:
+            return cb[0]
+        if v >= cb[-1]:
+            return cb[-1]
+        return min(cb, key=lambda c: (abs(v - c), c))
+    return q
+
+
+def sigma_delta_exact(x: Fraction, quantizer: Callable[[Fraction], Fraction],
+                      steps: int) -> Tuple[List[Fraction], List[Fraction]]:
+    """Run the recurrence from r_0 = 0 for ``steps`` accesses in exact
+    arithmetic; returns (q_1..q_R, r_1..r_R)."""
+    x = Fraction(x)
+    r = Fraction(0)
+    qs, rs = [], []
+    for _ in range(steps):
+        v = x + r
+        q = Fraction(quantizer(v))
+        r = v - q
+        qs.append(q)
+        rs.append(r)
+    return qs, rs
+
+
+def normalised_weight(w: np.ndarray):
+    """Fixed-scale setup of the NVFP4 chain for an fp32 master ``w`` [R, K]:
+    returns (x float32 [R, K], scale bytes, s_t, block_zero mask [R, K])."""
+    w = np.asarray(w, dtype=F32)
+    R, K = w.shape
+    _, sb_bytes, s_t = nvfp4.quantize(w)
+    s_b = e4m3_decode(sb_bytes).astype(F32)
+    s = (s_t * s_b).astype(F32)
+    with np.errstate(divide="ignore"):
+        rho = (F32(1.0) / s).astype(F32)
+    x = (w * np.repeat(rho, nvfp4.BLOCK, axis=1)).astype(F32)
+    zero = np.repeat(s == 0, nvfp4.BLOCK, axis=1)
+    x = np.where(zero, F32(0), x)
+    x = np.clip(x, F32(-6.0), F32(6.0)).astype(F32)
+    return x, sb_bytes, s_t, zero
+
+
+def sigma_delta_nvfp4(w: np.ndarray, steps: int, r0: np.ndarray = None):
+    """Run ``steps`` Sigma-Delta accesses on the fp32 master ``w`` [R, K].
+
+    Returns a dict with ``codes`` (list of uint8 [R, K] per step, unpacked),
+    ``residues`` (list of float32 [R, K] after each step), ``scales``
+    (E4M3 bytes [R, K/16]) and ``s_t``.  ``r0`` (float32) continues a chain
+    from a saved residue; default zeros.
+    """
+    x, sb_bytes, s_t, zero = normalised_weight(w)
+    r = np.zeros_like(x) if r0 is None else np.asarray(r0, dtype=F32).copy()
+    codes_all, res_all = [], []
+    for _ in range(steps):
+        v = (x + r).astype(F32)
+        codes = e2m1_round(v)
+        codes[zero] = 0
+        r64 = v.astype(np.float64) - e2m1_decode(codes)
+        r_new = r64.astype(F32)
+        assert np.array_equal(r_new.astype(np.float64), r64), "residue not exact in fp32"
+        r = r_new
+        codes_all.append(codes)
+        res_all.append(r.copy())
+    return {"codes": codes_all, "residues": res_all, "scales": sb_bytes, "s_t": s_t}

@@ -1,0 +1,224 @@
+"""Pins for the oracle's NVFP4 / MXFP4 quantizers, the block-32 Hadamard
+transform and the balance scale (CPU only)."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import formats as F, nvfp4, mxfp4, balance
+from block_scaled_fp4_mxfp4_amd import synth
+
+F32 = np.float32
+
+
+# ------------------------------------------------------------------ NVFP4 --
+
+def test_nvfp4_tensor_scale_is_amax_over_1536():
+    # loopquant page section 2.2: s_tensor = max|W| / (6 * 256)
+    x = synth.normal_f32(11, (8, 64), 3.0)
+    _, _, st = nvfp4.quantize(x)
+    a = np.abs(x).max()
+    assert st == F32(a / F32(1536))
+    assert abs(float(st) * 1536 / float(a) - 1) < 2 ** -23
+
+
+def test_nvfp4_block_scale_is_smallest_e4m3_at_least_amax_over_6st():
+    x = synth.heavy_tailed_f32(12, 13, (32, 256))
+    codes, sb, st = nvfp4.quantize(x)
+    table = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
+    a_b = np.abs(x).reshape(32, 16, 16).max(-1)
+    for i in range(32):
+        for j in range(16):
+            y = float(F32(a_b[i, j] / F32(F32(6) * st)))
+            want = np.nonzero(table >= y)[0][0]
+            assert sb[i, j] == want
+
+
+def test_nvfp4_codes_are_nearest_to_normalised_value():
+    x = synth.heavy_tailed_f32(14, 15, (16, 128))
+    codes, sb, st = nvfp4.quantize(x)
+    s = (st * F.e4m3_decode(sb).astype(F32)).astype(F32)
+    rho = (F32(1) / s).astype(F32)
+    mags = [Fraction(m) for m in (0, .5, 1, 1.5, 2, 3, 4, 6)]
+    exact_mismatch = 0
+    for i in range(16):
+        for k in range(128):
+            v = Fraction(float(F32(x[i, k] * rho[i, k // 16])))
+            want = min(range(8), key=lambda m: (abs(abs(v) - mags[m]), m & 1))
+            assert codes[i, k] & 7 == want
+            # against the exact quotient x / s (no reciprocal rounding)
+            vq = Fraction(float(x[i, k])) / Fraction(float(s[i, k // 16]))
+            wq = min(range(8), key=lambda m: (abs(abs(vq) - mags[m]), m & 1))
+            exact_mismatch += int(wq != want)
+    assert exact_mismatch == 0
+
+
+def test_nvfp4_normalised_magnitude_bounded_by_6():
+    # loopquant page section 2.2: the rounded-up E4M3 block scale keeps |x/s| <= 6
+    x = synth.heavy_tailed_f32(16, 17, (64, 512))
+    codes, sb, st = nvfp4.quantize(x)
+    s = st * F.e4m3_decode(sb)
+    v = np.abs(x.astype(np.float64)) / np.repeat(s, 16, axis=1)
+    assert v.max() <= 6 * (1 + 2 ** -21)
+
+
+def test_nvfp4_block_max_maps_to_six_when_scale_is_normal():
+    # ceil to E4M3 loses at most one part in 8 for normal E4M3 scales, so the
+    # block maximum lands in (5.33, 6] -> code magnitude 6
+    x = synth.heavy_tailed_f32(18, 19, (64, 512))
+    codes, sb, st = nvfp4.quantize(x)
+    blocks = np.abs(x).reshape(64, 32, 16)
+    cb = codes.reshape(64, 32, 16)
+    normal = F.e4m3_decode(sb) >= 2 ** -6
+    arg = blocks.argmax(-1)
+    top = np.take_along_axis(cb, arg[..., None], -1)[..., 0] & 7
+    assert np.all(top[normal] == 7)
+
+
+def test_nvfp4_block_max_over_rms_at_most_4():
+    # GDN page, background box "NVFP4 and W4A4": block max/RMS <= 4 in a
+    # 16-element block (= sqrt(16)); equality iff one non-zero element
+    x = synth.f32_to_bf16_bits(synth.heavy_tailed_f32(20, 21, (256, 1024)))
+    x = F.bf16_bits_to_f32(x).astype(np.float64).reshape(256, -1, 16)
+    r = np.abs(x).max(-1) / np.sqrt((x * x).mean(-1))
+    assert r.max() <= 4 + 1e-12
+    one = np.zeros((1, 16)); one[0, 5] = 3.0
+    assert np.abs(one).max() / np.sqrt((one ** 2).mean()) == 4.0
+
+
+def test_nvfp4_storage_is_4_5_bits():
+    # MACaQ page, image-diffusion comparison: NVFP4 costs 4.50 bits/element
+    x = synth.normal_f32(22, (4, 256))
+    codes, sb, _ = nvfp4.quantize(x)
+    packed = F.pack_nibbles(codes)
+    assert (packed.nbytes + sb.nbytes) * 8 / x.size == 4.5
+
+
+def test_nvfp4_exactly_representable_tensor_round_trips():
+    grid = np.array([6, 4, 3, 2, 1.5, 1, .5, 0, -.5, -1, -1.5, -2, -3, -4, -6, 0], F32)
+    for k in (-20, -3, 0, 5, 30):
+        x = np.tile(grid * F32(2.0 ** k), (3, 4)).astype(F32)
+        codes, sb, st = nvfp4.quantize(x)
+        assert np.array_equal(nvfp4.dequantize(codes, sb, st), x.astype(np.float64))
+        assert np.all(F.e4m3_decode(sb) == 256.0)
+
+
+def test_nvfp4_zero_tensor_and_given_scale():
+    z = np.zeros((2, 32), F32)
+    codes, sb, st = nvfp4.quantize(z)
+    assert st == 0 and not codes.any() and not sb.any()
+    x = synth.normal_f32(23, (2, 32))
+    c1, s1, st1 = nvfp4.quantize(x)
+    c2, s2, st2 = nvfp4.quantize(x, tensor_scale=st1)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2) and st1 == st2
+    c3, s3, st3 = nvfp4.quantize(x, tensor_scale=F32(0))
+    assert not c3.any() and not s3.any()
+
+
+def test_nvfp4_error_in_plausible_range():
+    # sanity only: the GDN page reports A4 errors of 7.5-9.2 % on real data
+    x = synth.heavy_tailed_f32(24, 25, (256, 1024))
+    codes, sb, st = nvfp4.quantize(x)
+    d = nvfp4.dequantize(codes, sb, st) - x
+    e = np.linalg.norm(d) / np.linalg.norm(x)
+    assert 0.04 < e < 0.15
+
+
+# ------------------------------------------------------------- Hadamard --
+
+def test_sylvester_hadamard_is_orthogonal():
+    H = scipy.linalg.hadamard(32)
+    assert np.array_equal(H @ H.T, 32 * np.eye(32, dtype=H.dtype))
+    assert set(np.unique(H)) == {-1, 1}
+
+
+def test_fwht_matches_dense_sylvester_exactly_on_integers():
+    H = scipy.linalg.hadamard(32).astype(np.float64)
+    rng = np.random.default_rng(5)
+    z = rng.integers(-1000, 1000, size=(20, 96)).astype(F32)
+    y = mxfp4.fwht32_stages(z).astype(np.float64)
+    ref = (z.astype(np.float64).reshape(20, 3, 32) @ H.T).reshape(20, 96)
+    assert np.array_equal(y, ref)
+
+
+def test_fwht_matches_dense_on_floats():
+    H = scipy.linalg.hadamard(32).astype(np.float64) / np.sqrt(32)
+    x = synth.heavy_tailed_f32(26, 27, (16, 256))
+    y = mxfp4.hadamard32_scale(x).astype(np.float64)
+    ref = (x.astype(np.float64).reshape(16, 8, 32) @ H.T).reshape(16, 256)
+    assert np.abs(y - ref).max() <= 1e-5 * np.abs(ref).max()
+    # orthonormal and symmetric -> applying it twice is the identity
+    yy = mxfp4.hadamard32_scale(mxfp4.hadamard32_scale(x)).astype(np.float64)
+    assert np.abs(yy - x).max() <= 1e-5 * np.abs(x).max()
+
+
+def test_scale_then_rotate_leaves_product_unchanged():
+    # MACaQ page, core method (ii): X' D B (W D^-1 B)^T = X W^T
+    x = synth.heavy_tailed_f32(28, 29, (32, 256))
+    w = synth.normal_f32(30, (48, 256), 0.02)
+    t64, t32, u32 = balance.balance_scale(w, x)
+    xp = mxfp4.hadamard32_scale(x, t32).astype(np.float64)
+    wp = mxfp4.hadamard32_scale(w, u32).astype(np.float64)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    got = xp @ wp.T
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-5
+
+
+# ---------------------------------------------------------------- MXFP4 --
+
+def test_mxfp4_scale_is_power_of_two_with_block_max_in_4_8():
+    y = synth.heavy_tailed_f32(31, 32, (32, 512))
+    codes, sc = mxfp4.quantize(y)
+    a_b = np.abs(y.astype(np.float64)).reshape(32, 16, 32).max(-1)
+    s = F.e8m0_decode(sc)
+    ratio = a_b / s
+    assert np.all((ratio >= 4) & (ratio < 8))
+    tt = torch.from_numpy(sc.copy()).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(tt, s)
+
+
+def test_mxfp4_codes_nearest_and_saturate():
+    y = synth.heavy_tailed_f32(33, 34, (8, 128))
+    codes, sc = mxfp4.quantize(y)
+    mags = [Fraction(m) for m in (0, .5, 1, 1.5, 2, 3, 4, 6)]
+    for i in range(8):
+        for k in range(128):
+            v = Fraction(float(y[i, k])) / (Fraction(2) ** (int(sc[i, k // 32]) - 127))
+            want = min(range(8), key=lambda m: (abs(abs(v) - mags[m]), m & 1))
+            assert codes[i, k] & 7 == want
+
+
+def test_mxfp4_storage_is_4_25_bits_and_zero_block():
+    # MACaQ page, MXFP4 box: about 4.25 bits per element
+    y = synth.normal_f32(35, (4, 256))
+    y[1, 32:64] = 0
+    codes, sc = mxfp4.quantize(y)
+    assert (F.pack_nibbles(codes).nbytes + sc.nbytes) * 8 / y.size == 4.25
+    assert sc[1, 1] == 0 and not codes[1, 32:64].any()
+
+
+def test_mxfp4_subnormal_and_extreme_blocks():
+    y = np.zeros((1, 96), F32)
+    y[0, 0] = np.float32(1e-45)                  # smallest subnormal
+    y[0, 32] = np.float32(3e38)                  # near the fp32 max
+    y[0, 64:96] = F32(6.0)
+    codes, sc = mxfp4.quantize(y)
+    assert sc[0, 0] == 0                         # exponent clamped at -127
+    assert sc[0, 1] == 127 + 127 - 2             # floor(log2 3e38) = 127
+    # a block of 6.0: floor(log2 6) = 2 -> e = 0 -> v = 6 -> magnitude index 7
+    assert sc[0, 2] == 127 and np.all(codes[0, 64:96] == 0x7)
+    assert mxfp4.dequantize(codes, sc)[0, 0] == 0.0
+
+
+def test_balance_scale_closed_form():
+    rng = np.random.default_rng(36)
+    w = rng.standard_normal((50, 4)) * np.array([1.0, 2.0, 0.5, 4.0])
+    x = rng.standard_normal((70, 4)) * np.array([3.0, 1.0, 10.0, 0.25])
+    t64, t32, u32 = balance.balance_scale(w, x)
+    sig = np.sqrt(((w - w.mean(0)) ** 2).mean(0))
+    rms = np.sqrt((x ** 2).mean(0))
+    assert np.allclose(t64, sig ** 0.75 / rms ** 0.25, rtol=1e-14)
+    assert t32.dtype == np.float32 and u32.dtype == np.float32
+    assert np.allclose(t32.astype(np.float64) * u32, 1, rtol=2e-7)

@@ -1,0 +1,154 @@
+"""Pins for the oracle's Sigma-Delta recurrence and its GEMMs (CPU only)."""
+import os
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+
+from oracle import formats as F, nvfp4, mxfp4, sigma_delta as SD, gemm
+from block_scaled_fp4_mxfp4_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _golden_rows(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append([Fraction(t) for t in line.split()])
+    return out
+
+
+def test_worked_example_x03_integer_grid():
+    # loopquant page, section 2.1: x = 0.3, integer grid, floor(v + 1/2)
+    q_int = lambda v: Fraction(math.floor(v + Fraction(1, 2)))
+    qs, rs = SD.sigma_delta_exact(Fraction(3, 10), q_int, 8)
+    rows = _golden_rows("sigma_delta_x03.txt")
+    x = Fraction(3, 10)
+    prefix = Fraction(0)
+    for k, (row, q, r) in enumerate(zip(rows, qs, rs), start=1):
+        kk, v, qq, rr, pe = row
+        assert kk == k and q == qq and r == rr
+        prefix += q - x
+        assert prefix == pe == -r                 # prefix error = -r_k
+        assert abs(r) <= Fraction(1, 2)
+    # static RTN: 0 every step, error -0.3 each step, diverging linearly
+    assert all(q_int(x) == 0 for _ in range(8))
+
+
+def test_telescoping_and_bound_on_random_code_books():
+    rng = np.random.default_rng(40)
+    for trial in range(60):
+        n = int(rng.integers(2, 9))
+        cb = sorted(set(Fraction(int(v), int(rng.integers(1, 5)))
+                        for v in rng.integers(-20, 20, size=n)))
+        if len(cb) < 2:
+            continue
+        d = max(b - a for a, b in zip(cb, cb[1:]))
+        x = cb[0] + (cb[-1] - cb[0]) * Fraction(int(rng.integers(0, 1000)), 999)
+        qs, rs = SD.sigma_delta_exact(x, SD.nearest_saturating(cb), 50)
+        s = Fraction(0)
+        for m, (q, r) in enumerate(zip(qs, rs), start=1):
+            s += q - x
+            assert s == -r                       # section 2.1 telescoping
+            assert abs(r) <= d / 2               # section 2.2 bound
+            assert abs(s / m) <= d / (2 * m)     # mean error <= d / (2m)
+
+
+def test_divergence_outside_hull():
+    # section 2.2: C = {0, 1}, x = 2 -> residue grows without bound
+    qs, rs = SD.sigma_delta_exact(Fraction(2), SD.nearest_saturating([0, 1]), 10)
+    assert rs == [Fraction(k) for k in range(1, 11)]
+
+
+def test_e2m1_code_book_bound_is_one():
+    cb = sorted(set(Fraction(float(v)) for v in F.E2M1_VALUES))
+    rng = np.random.default_rng(41)
+    for _ in range(40):
+        x = Fraction(int(rng.integers(-6000, 6001)), 1000)
+        _, rs = SD.sigma_delta_exact(x, SD.nearest_saturating(cb), 32)
+        assert max(abs(r) for r in rs) <= 1
+
+
+def test_nvfp4_chain_step1_is_rtn_and_bound_holds():
+    w = synth.normal_f32(42, (48, 256), 0.02)
+    w[3, 16:32] = 0.0                                        # a zero block
+    out = SD.sigma_delta_nvfp4(w, 32)
+    codes_rtn, sb, st = nvfp4.quantize(w)
+    # loopquant page, section 2.3: the first code of the chain is the RTN code
+    assert np.array_equal(out["codes"][0], codes_rtn)
+    assert np.array_equal(out["scales"], sb) and out["s_t"] == st
+    for r in out["residues"]:
+        assert np.abs(r).max() <= 1.0                        # |r_k| <= d/2 = 1
+    assert not any(c[3, 16:32].any() for c in out["codes"])
+
+
+def test_nvfp4_chain_telescopes_within_fp32_rounding():
+    w = synth.normal_f32(43, (16, 128), 0.02)
+    out = SD.sigma_delta_nvfp4(w, 32)
+    x, _, _, _ = SD.normalised_weight(w)
+    x = x.astype(np.float64)
+    acc = np.zeros_like(x)
+    for m, (c, r) in enumerate(zip(out["codes"], out["residues"]), start=1):
+        acc += F.e2m1_decode(c) - x
+        # each v = fl(x + r) rounds by at most half an ulp of 8 (2**-21)
+        assert np.abs(acc + r.astype(np.float64)).max() <= m * 2.0 ** -21
+        assert np.abs(acc / m).max() <= 1.0 / m + 2.0 ** -21
+
+
+def test_nvfp4_chain_resume_is_exact():
+    w = synth.normal_f32(44, (8, 64), 0.02)
+    full = SD.sigma_delta_nvfp4(w, 12)
+    a = SD.sigma_delta_nvfp4(w, 5)
+    b = SD.sigma_delta_nvfp4(w, 7, r0=a["residues"][-1])
+    for k in range(7):
+        assert np.array_equal(full["codes"][5 + k], b["codes"][k])
+        assert np.array_equal(full["residues"][5 + k], b["residues"][k])
+
+
+# ------------------------------------------------------------------ GEMM --
+
+def test_gemm_one_hot_rows_return_weight_rows():
+    w = synth.normal_f32(45, (24, 64), 0.02)
+    bc, bs, bst = nvfp4.quantize(w)
+    a = np.zeros((3, 64), F32)
+    a[0, 5] = 1.0; a[1, 63] = 1.0; a[2, 0] = -1.0
+    ac, as_, ast = nvfp4.quantize(a)
+    y = gemm.w4a4_nvfp4(ac, as_, ast, bc, bs, bst)
+    wd = nvfp4.dequantize(bc, bs, bst)
+    ad = nvfp4.dequantize(ac, as_, ast)
+    # a one-hot row dequantizes to a single non-zero (6 * s_b * s_t, not
+    # exactly 1 because s_t = 1/1536 rounds in fp32)
+    assert np.count_nonzero(ad[0]) == 1 and abs(ad[0, 5] - 1) < 1e-6
+    assert np.array_equal(y[0], ad[0, 5] * wd[:, 5]) and np.array_equal(y[1], ad[1, 63] * wd[:, 63])
+    assert np.array_equal(y[2], ad[2, 0] * wd[:, 0])
+
+
+def test_gemm_matches_exact_rational_brute_force():
+    x = synth.heavy_tailed_f32(46, 47, (4, 64))
+    w = synth.normal_f32(48, (5, 64), 0.02)
+    ac, as_, ast = nvfp4.quantize(x)
+    bc, bs, bst = nvfp4.quantize(w)
+    y = gemm.w4a4_nvfp4(ac, as_, ast, bc, bs, bst)
+    A = nvfp4.dequantize(ac, as_, ast)
+    B = nvfp4.dequantize(bc, bs, bst)
+    for i in range(4):
+        for j in range(5):
+            ex = sum(Fraction(float(A[i, k])) * Fraction(float(B[j, k])) for k in range(64))
+            assert abs(Fraction(float(y[i, j])) - ex) <= sum(abs(Fraction(float(A[i, k])) * Fraction(float(B[j, k]))) for k in range(64)) * Fraction(64, 2 ** 53) + Fraction(1, 2 ** 200)
+    # MXFP4 and W4A16 variants on the same data
+    mc, ms = mxfp4.quantize(x); wc, ws = mxfp4.quantize(w)
+    ym = gemm.w4a4_mxfp4(mc, ms, wc, ws)
+    assert np.allclose(ym, mxfp4.dequantize(mc, ms) @ mxfp4.dequantize(wc, ws).T, rtol=0, atol=0)
+    xb = synth.f32_to_bf16_bits(x)
+    yh = gemm.w4a16(xb, bc, bs, bst)
+    assert np.allclose(yh, F.bf16_bits_to_f32(xb).astype(np.float64) @ B.T, rtol=0, atol=0)
+
+
+def test_rel_err_metric():
+    y = np.array([[1.0, 0.0], [0.0, 2.0]])
+    whole, row, mx = gemm.rel_err(y * (1 + 1e-4), y)
+    assert abs(whole - 1e-4) < 1e-12 and abs(row - 1e-4) < 1e-12 and abs(mx - 1e-4) < 1e-12
