@@ -1,0 +1,601 @@
+// gemm.hip -- W4A4 and W4A16 GEMMs of libfp4q for gfx950 (CDNA4).
+//
+//   Y[M][N] = dequant(A)[M][K] * dequant(B)[N][K]^T, fp32 accumulate / output.
+//
+// MXFP4 ("MACaQ", core method: y = [(x*t)B]_MXFP4 W'^T_MXFP4): the packed
+// E2M1 codes go straight into the block-scaled FP4 matrix core instruction
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0 bytes as its per-lane,
+// per-32-element scale operands -- the OCP MXFP4 block is exactly the
+// instruction's scale block.
+//
+// NVFP4 ("Why Gated DeltaNet Survives 4-Bit Quantization", box "NVFP4 and
+// W4A4"): the E4M3 scale belongs to a 16-element block and has a 3-bit
+// mantissa, so it cannot ride the instruction's E8M0 scale.  Instead each
+// element is dequantized EXACTLY to fp16 in registers: value(code) * 2^e
+// with one v_cvt_scalef32_pk_f16_fp4 (the instruction applies the power of
+// two), then times the scale mantissa (1 + f/8, or f for subnormal E4M3) with
+// v_pk_mul_f16.  code * s_b has at most 2 + 4 significant bits and lies in
+// [2^-10, 2688], so fp16 holds it exactly; the fp16 matrix core
+// (v_mfma_f32_16x16x32_f16) multiplies exact values and accumulates in fp32.
+// The two fp32 tensor scales are applied once in the epilogue.
+//
+// W4A16 (looped core: bf16 hidden state times the re-quantized weight): the
+// weight is dequantized exactly to bf16 (fp32 value(code) * s_b, exact, then
+// its upper half) and multiplied on the bf16 matrix core.
+//
+// Tiling (prefill kernels): 128 x 128 output tile per 256-thread workgroup,
+// 2 x 2 wavefronts of 64 x 64, K staged 128 elements at a time through LDS
+// with register double buffering.  Within a 128-element stage the 16 lanes
+// of lane group g (= lane / 16) own elements [32g, 32g + 32) of their row,
+// which is the FP4 instruction's own layout; the fp16 / bf16 instructions
+// consume those 32 elements as four 8-element slices, one per instruction.
+// A and B use the same assignment, so the dot product is unchanged.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.h"
+#include "internal.h"
+
+namespace fp4q {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int BM = 128, BN = 128;
+constexpr int BK = 128;           // K elements per stage
+constexpr int BKB = BK / 2;       // code bytes per row per stage
+constexpr int LDR = BKB + 16;     // padded LDS row stride of a code tile (bytes)
+
+// ------------------------------------------------------------ dequant ----
+
+// E4M3 block scale split into a power of two (for the convert instruction)
+// and an fp16 mantissa factor: s_b = pow2 * m exactly.
+struct ScaleSplit {
+  float pow2;
+  v2h m;
+};
+
+__device__ __forceinline__ ScaleSplit split_e4m3(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xFu, f = b & 7u;
+  ScaleSplit s;
+  if (e) {
+    s.pow2 = __uint_as_float((e + 120u) << 23);                 // 2^(e-7)
+    const _Float16 m = (_Float16)(1.0f + 0.125f * (float)f);     // exact
+    s.m = v2h{m, m};
+  } else {
+    s.pow2 = __uint_as_float(118u << 23);                       // 2^-9
+    const _Float16 m = (_Float16)(float)f;
+    s.m = v2h{m, m};
+  }
+  return s;
+}
+
+// 8 codes (one dword, element 2i in the low nibble of byte i) -> 8 exact fp16.
+__device__ __forceinline__ v8h dequant8_f16(uint32_t w, const ScaleSplit& s) {
+  uint32_t o[4];
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 0)) * s.m);
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 1)) * s.m);
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 2)) * s.m);
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 3)) * s.m);
+  return __builtin_bit_cast(v8h, uint4{o[0], o[1], o[2], o[3]});
+}
+
+// 8 codes -> 8 exact bf16: value(code) in fp32, times s_b (exact), upper half.
+__device__ __forceinline__ v8bf dequant8_bf16(uint32_t w, float sb) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo, hi;
+    switch (i) {
+      case 0: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); lo = p[0]; hi = p[1]; break; }
+      case 1: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); lo = p[0]; hi = p[1]; break; }
+      case 2: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); lo = p[0]; hi = p[1]; break; }
+      default: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); lo = p[0]; hi = p[1]; break; }
+    }
+    lo = lo * sb;
+    hi = hi * sb;
+    o[i] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
+  return __builtin_bit_cast(v8bf, uint4{o[0], o[1], o[2], o[3]});
+}
+
+// ------------------------------------------------- stage load helpers ----
+
+// Copies rows [r0, r0 + 128) x 64 code bytes of stage kt into registers
+// (two 16-byte chunks per thread); rows past `rows` read as zero.
+struct CodeStage {
+  uint4 q[2];
+};
+
+__device__ __forceinline__ void load_code_stage(CodeStage& st, const uint8_t* __restrict__ g,
+                                                int64_t r0, int64_t rows, int64_t ldb, int kt) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    const int64_t r = r0 + (c >> 2);
+    st.q[i] = r < rows ? *reinterpret_cast<const uint4*>(g + r * ldb + (int64_t)kt * BKB + (c & 3) * 16)
+                       : uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void store_code_stage(const CodeStage& st, uint8_t* l) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    *reinterpret_cast<uint4*>(l + (c >> 2) * LDR + (c & 3) * 16) = st.q[i];
+  }
+}
+
+// ============================================================ MXFP4 ====
+
+__global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, int64_t M, int64_t N, int64_t K, float* __restrict__ Y,
+    int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDR];
+  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDR];
+  __shared__ uint32_t lS[2][BM + BN];          // 4 E8M0 bytes per row per stage
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int64_t ldb = K / 2, lds = K / 32;
+  const int KT = (int)(K / BK);
+
+  CodeStage sa, sb;
+  uint32_t ss = 0;
+  auto gload = [&](int kt) {
+    load_code_stage(sa, A, m0, M, ldb, kt);
+    load_code_stage(sb, B, n0, N, ldb, kt);
+    if (tid < BM) {
+      const int64_t r = m0 + tid;
+      ss = r < M ? *reinterpret_cast<const uint32_t*>(As + r * lds + kt * 4) : 0u;
+    } else {
+      const int64_t r = n0 + tid - BM;
+      ss = r < N ? *reinterpret_cast<const uint32_t*>(Bs + r * lds + kt * 4) : 0u;
+    }
+  };
+  auto sstore = [&](int buf) {
+    store_code_stage(sa, lA[buf]);
+    store_code_stage(sb, lB[buf]);
+    lS[buf][tid] = ss;
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    v8i af[4], bfr[4];
+    int sca[4], scb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * 64 + i * 16 + r16;
+      const uint4 qa = *reinterpret_cast<const uint4*>(&lA[buf][ra * LDR + g * 16]);
+      af[i] = v8i{(int)qa.x, (int)qa.y, (int)qa.z, (int)qa.w, 0, 0, 0, 0};
+      sca[i] = (int)((lS[buf][ra] >> (8 * g)) & 0xFFu);
+      const int rb = wn * 64 + i * 16 + r16;
+      const uint4 qb = *reinterpret_cast<const uint4*>(&lB[buf][rb * LDR + g * 16]);
+      bfr[i] = v8i{(int)qb.x, (int)qb.y, (int)qb.z, (int)qb.w, 0, 0, 0, 0};
+      scb[i] = (int)((lS[buf][BM + rb] >> (8 * g)) & 0xFFu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bfr[j], acc[i][j], 4, 4, 0,
+                                                                     sca[i], 0, scb[j]);
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 16 + g * 4 + r;
+        const int64_t col = n0 + wn * 64 + j * 16 + r16;
+        if (row < M && col < N) Y[row * ldy + col] = acc[i][j][r];
+      }
+}
+
+// ============================================================ NVFP4 ====
+
+__global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
+    int64_t M, int64_t N, int64_t K, float* __restrict__ Y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDR];
+  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDR];
+  __shared__ uint2 lS[2][BM + BN];             // 8 E4M3 bytes per row per stage
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int64_t ldb = K / 2, lds = K / 16;
+  const int KT = (int)(K / BK);
+
+  CodeStage sa, sb;
+  uint2 ss = {0u, 0u};
+  auto gload = [&](int kt) {
+    load_code_stage(sa, A, m0, M, ldb, kt);
+    load_code_stage(sb, B, n0, N, ldb, kt);
+    if (tid < BM) {
+      const int64_t r = m0 + tid;
+      ss = r < M ? *reinterpret_cast<const uint2*>(As + r * lds + kt * 8) : uint2{0u, 0u};
+    } else {
+      const int64_t r = n0 + tid - BM;
+      ss = r < N ? *reinterpret_cast<const uint2*>(Bs + r * lds + kt * 8) : uint2{0u, 0u};
+    }
+  };
+  auto sstore = [&](int buf) {
+    store_code_stage(sa, lA[buf]);
+    store_code_stage(sb, lB[buf]);
+    lS[buf][tid] = ss;
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    uint4 qa[4], qb[4];
+    ScaleSplit xa[4][2], xb[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * 64 + i * 16 + r16;
+      qa[i] = *reinterpret_cast<const uint4*>(&lA[buf][ra * LDR + g * 16]);
+      const uint2 sa2 = lS[buf][ra];
+      const uint32_t wa = (g < 2 ? sa2.x : sa2.y) >> (16 * (g & 1));
+      xa[i][0] = split_e4m3(wa & 0xFFu);
+      xa[i][1] = split_e4m3((wa >> 8) & 0xFFu);
+      const int rb = wn * 64 + i * 16 + r16;
+      qb[i] = *reinterpret_cast<const uint4*>(&lB[buf][rb * LDR + g * 16]);
+      const uint2 sb2 = lS[buf][BM + rb];
+      const uint32_t wb = (g < 2 ? sb2.x : sb2.y) >> (16 * (g & 1));
+      xb[i][0] = split_e4m3(wb & 0xFFu);
+      xb[i][1] = split_e4m3((wb >> 8) & 0xFFu);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8h ha[4], hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
+        const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
+        ha[i] = dequant8_f16(wa, xa[i][s >> 1]);
+        hb[i] = dequant8_f16(wb, xb[i][s >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i], hb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  const float tsc = (*Ats) * (*Bts);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 16 + g * 4 + r;
+        const int64_t col = n0 + wn * 64 + j * 16 + r16;
+        if (row < M && col < N) Y[row * ldy + col] = acc[i][j][r] * tsc;
+      }
+}
+
+// ============================================================ W4A16 ====
+
+constexpr int LDA16 = BK * 2 + 16;   // padded LDS row stride of a bf16 A stage (bytes)
+
+__global__ __launch_bounds__(kThreads) void k_gemm_w4a16(
+    const uint16_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const float* __restrict__ Bts, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ Y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDA16];
+  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDR];
+  __shared__ uint2 lS[2][BN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int64_t ldb = K / 2, lds = K / 16;
+  const int KT = (int)(K / BK);
+
+  uint4 ra[8];
+  CodeStage sb;
+  uint2 ss = {0u, 0u};
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {         // 128 rows x 256 bytes = 2048 chunks
+      const int c = tid + kThreads * i;
+      const int64_t r = m0 + (c >> 4);
+      ra[i] = r < M ? *reinterpret_cast<const uint4*>(A + r * lda + (int64_t)kt * BK + (c & 15) * 8)
+                    : uint4{0u, 0u, 0u, 0u};
+    }
+    load_code_stage(sb, B, n0, N, ldb, kt);
+    if (tid < BN) {
+      const int64_t r = n0 + tid;
+      ss = r < N ? *reinterpret_cast<const uint2*>(Bs + r * lds + kt * 8) : uint2{0u, 0u};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4*>(&lA[buf][(c >> 4) * LDA16 + (c & 15) * 16]) = ra[i];
+    }
+    store_code_stage(sb, lB[buf]);
+    if (tid < BN) lS[buf][tid] = ss;
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    uint4 qb[4];
+    float sbv[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rb = wn * 64 + j * 16 + r16;
+      qb[j] = *reinterpret_cast<const uint4*>(&lB[buf][rb * LDR + g * 16]);
+      const uint2 s2 = lS[buf][rb];
+      const uint32_t w = (g < 2 ? s2.x : s2.y) >> (16 * (g & 1));
+      sbv[j][0] = e4m3_decode(w & 0xFFu);
+      sbv[j][1] = e4m3_decode((w >> 8) & 0xFFu);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8bf ha[4], hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra_ = wm * 64 + i * 16 + r16;
+        ha[i] = *reinterpret_cast<const v8bf*>(&lA[buf][ra_ * LDA16 + (32 * g + 8 * s) * 2]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = s == 0 ? qb[j].x : s == 1 ? qb[j].y : s == 2 ? qb[j].z : qb[j].w;
+        hb[j] = dequant8_bf16(w, sbv[j][s >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[i], hb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  const float tsc = *Bts;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 16 + g * 4 + r;
+        const int64_t col = n0 + wn * 64 + j * 16 + r16;
+        if (row < M && col < N) Y[row * ldy + col] = acc[i][j][r] * tsc;
+      }
+}
+
+// ================================================== skinny NVFP4 (M<=16) ====
+//
+// Decode-shaped: the weight is streamed once from HBM, so it is read straight
+// into registers (no LDS staging).  A (<= 16 rows) lives in LDS as codes and
+// E4M3 scales, either copied (pre-quantized) or quantized in the prologue
+// with the recipe of fp4q_quantize_nvfp4 (fused).  Each workgroup owns 64
+// weight rows; its four wavefronts split K and their partial 16 x 64 tiles
+// are summed in a fixed order through LDS, so the fused and unfused entries
+// produce identical Y.
+
+constexpr int SK_MAXK = 7168;   // A codes + scales (9K bytes) within 64 KiB of LDS
+constexpr uint32_t kAmaxFlag = 0x80000000u;
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kThreads) void k_gemm_nvfp4_skinny(
+    const uint16_t* __restrict__ Abf, int64_t lda, const uint8_t* __restrict__ Ac,
+    const uint8_t* __restrict__ As, float* Ats, int a_dynamic, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const float* __restrict__ Bts, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ Y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* lAc = smem;                          // [16][K/2]
+  uint8_t* lAs = smem + 16 * (K / 2);           // [16][K/16]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t ldb = K / 2, lds = K / 16;
+
+  float ats;
+  if constexpr (FUSED) {
+    // quantize A[0:M) exactly as k_quant_nvfp4 does; rows >= M become zero
+    const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(Ats));
+    ats = (a_dynamic && (u & kAmaxFlag)) ? __uint_as_float(u & 0x7FFFFFFFu) / 1536.0f : __uint_as_float(u);
+    const float six_st = 6.0f * ats;
+    const int64_t cpr = K / 8, nch = 16 * cpr;
+    for (int64_t c = tid; c < nch; c += kThreads) {
+      const int64_t r = c / cpr, c8 = c - r * cpr;
+      float v[8];
+      if (r < M) {
+        const uint4 q = *reinterpret_cast<const uint4*>(Abf + r * lda + c8 * 8);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(w[i] << 16);
+          v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+      a = fmaxf(a, dpp_xor1(a));
+      uint32_t sb = 0;
+      if (a > 0.0f && ats > 0.0f) sb = e4m3_ceil(a / six_st);
+      const float s = ats * e4m3_decode(sb);
+      const float rho = 1.0f / s;
+      uint32_t p = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p |= ((s == 0.0f) ? 0u : e2m1_encode(v[i] * rho)) << (4 * i);
+      *reinterpret_cast<uint32_t*>(lAc + r * (K / 2) + c8 * 4) = p;
+      if (!(c & 1)) lAs[r * lds + (c8 >> 1)] = (uint8_t)sb;
+    }
+    if (a_dynamic && blockIdx.x == 0 && tid == 0) *Ats = ats;
+  } else {
+    ats = *Ats;
+    const int64_t n16 = 16 * (K / 32);          // 16-byte chunks of A codes
+    for (int64_t c = tid; c < n16; c += kThreads) {
+      const int64_t r = c / (K / 32), cc = c - r * (K / 32);
+      const uint4 q = r < M ? *reinterpret_cast<const uint4*>(Ac + r * (K / 2) + cc * 16) : uint4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint4*>(lAc + r * (K / 2) + cc * 16) = q;
+    }
+    for (int64_t c = tid; c < 16 * lds; c += kThreads) {
+      const int64_t r = c / lds;
+      lAs[c] = r < M ? As[r * lds + (c - r * lds)] : (uint8_t)0;
+    }
+  }
+  __syncthreads();
+
+  // this wavefront's share of the K stages
+  const int KT = (int)(K / BK);
+  const int kt0 = (KT * wave) / 4, kt1 = (KT * (wave + 1)) / 4;
+  v4f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int kt = kt0; kt < kt1; ++kt) {
+    uint4 qb[4];
+    uint32_t wsb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t rn = n0 + j * 16 + r16;
+      if (rn < N) {
+        qb[j] = *reinterpret_cast<const uint4*>(B + rn * ldb + (int64_t)kt * BKB + g * 16);
+        wsb[j] = *reinterpret_cast<const uint16_t*>(Bs + rn * lds + kt * 8 + 2 * g);
+      } else {
+        qb[j] = uint4{0u, 0u, 0u, 0u};
+        wsb[j] = 0u;
+      }
+    }
+    const uint4 qa = *reinterpret_cast<const uint4*>(lAc + r16 * (K / 2) + kt * BKB + g * 16);
+    const uint32_t wsa = *reinterpret_cast<const uint16_t*>(lAs + r16 * lds + kt * 8 + 2 * g);
+    const ScaleSplit xa0 = split_e4m3(wsa & 0xFFu), xa1 = split_e4m3(wsa >> 8);
+    ScaleSplit xb[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xb[j][0] = split_e4m3(wsb[j] & 0xFFu);
+      xb[j][1] = split_e4m3(wsb[j] >> 8);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t wa = s == 0 ? qa.x : s == 1 ? qa.y : s == 2 ? qa.z : qa.w;
+      const v8h ha = dequant8_f16(wa, s < 2 ? xa0 : xa1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t wb = s == 0 ? qb[j].x : s == 1 ? qb[j].y : s == 2 ? qb[j].z : qb[j].w;
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha, dequant8_f16(wb, xb[j][s >> 1]), acc[j], 0, 0, 0);
+      }
+    }
+  }
+  // fixed-order reduction of the four K-partials
+  __syncthreads();                               // A tiles no longer needed
+  float* red = reinterpret_cast<float*>(smem);   // [4][16][64]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 16 + g * 4 + r) * 64 + j * 16 + r16] = acc[j][r];
+  __syncthreads();
+  const float tsc = ats * (*Bts);
+  for (int o = tid; o < 16 * 64; o += kThreads) {
+    const int m = o >> 6, n = o & 63;
+    const float v = ((red[(0 * 16 + m) * 64 + n] + red[(1 * 16 + m) * 64 + n]) + red[(2 * 16 + m) * 64 + n]) +
+                    red[(3 * 16 + m) * 64 + n];
+    if (m < M && n0 + n < N) Y[(int64_t)m * ldy + n0 + n] = v * tsc;
+  }
+}
+
+inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+}  // namespace
+
+hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
+                             int64_t ldy, hipStream_t s) {
+  hipLaunchKernelGGL(k_gemm_mxfp4, dim3(cdiv(N, BN), cdiv(M, BM)), dim3(kThreads), 0, s, a, as, b, bs, M,
+                     N, K, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
+                             const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
+                             int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s) {
+  hipLaunchKernelGGL(k_gemm_nvfp4, dim3(cdiv(N, BN), cdiv(M, BM)), dim3(kThreads), 0, s, a, as, ats, b,
+                     bs, bts, M, N, K, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
+                             const float* bts, int64_t M, int64_t N, int64_t K, float* y,
+                             int64_t ldy, hipStream_t s) {
+  hipLaunchKernelGGL(k_gemm_w4a16, dim3(cdiv(N, BN), cdiv(M, BM)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint16_t*>(a), lda, b, bs, bts, M, N, K, y, ldy);
+  return hipGetLastError();
+}
+
+bool skinny_supported(int64_t K) { return K <= SK_MAXK; }
+
+hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8_t* a_codes,
+                                    const uint8_t* a_scales, const float* a_ts, int a_dynamic,
+                                    const uint8_t* b, const uint8_t* bs, const float* bts,
+                                    int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
+                                    hipStream_t s) {
+  size_t a_bytes = 16 * (K / 2) + 16 * (K / 16);
+  const size_t red_bytes = 4 * 16 * 64 * sizeof(float);
+  const size_t shm = a_bytes > red_bytes ? a_bytes : red_bytes;
+  if (a_bf16)
+    hipLaunchKernelGGL((k_gemm_nvfp4_skinny<true>), dim3(cdiv(N, 64)), dim3(kThreads), shm, s,
+                       reinterpret_cast<const uint16_t*>(a_bf16), lda, nullptr, nullptr,
+                       const_cast<float*>(a_ts), a_dynamic, b, bs, bts, M, N, K, y, ldy);
+  else
+    hipLaunchKernelGGL((k_gemm_nvfp4_skinny<false>), dim3(cdiv(N, 64)), dim3(kThreads), shm, s, nullptr,
+                       (int64_t)0, a_codes, a_scales, const_cast<float*>(a_ts), 0, b, bs, bts, M, N, K, y, ldy);
+  return hipGetLastError();
+}
+
+}  // namespace fp4q

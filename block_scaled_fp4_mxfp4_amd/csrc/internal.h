@@ -1,0 +1,50 @@
+// internal.h -- launchers shared between the kernel translation units and the
+// C ABI layer (api.cpp).  Every launcher enqueues on `s` and returns the HIP
+// status of its launches; argument validation happens in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp4q.h"
+
+namespace fp4q {
+
+hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
+                              hipStream_t s);
+hipError_t launch_amax_to_cell(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
+                               float* cell, hipStream_t s);
+hipError_t launch_quant_mxfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
+                              const float* chan_scale, int hadamard, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+hipError_t launch_hadamard32_scale(const void* x, int bf16, int64_t rows, int64_t cols,
+                                   int64_t ldx, const float* chan_scale, float* y, int64_t ldy,
+                                   hipStream_t s);
+hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K, int64_t ldw,
+                                const void* x, int x_bf16, int64_t M, int64_t ldx, double alpha,
+                                float* t_out, float* u_out, hipStream_t s);
+hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
+                              int64_t bank_stride, hipStream_t s);
+
+hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
+                             int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
+                             const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
+                             int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
+                             const float* bts, int64_t M, int64_t N, int64_t K, float* y,
+                             int64_t ldy, hipStream_t s);
+// Largest K the skinny kernel holds in LDS.
+bool skinny_supported(int64_t K);
+// Skinny NVFP4 GEMM for M <= 16.  If a_bf16 != NULL the activation is
+// quantized inside the kernel (a_codes / a_scales ignored; a_ts is the
+// tensor-scale cell in the same state encoding fp4q_quantize_nvfp4 uses).
+hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8_t* a_codes,
+                                    const uint8_t* a_scales, const float* a_ts, int a_dynamic,
+                                    const uint8_t* b, const uint8_t* bs, const float* bts,
+                                    int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
+                                    hipStream_t s);
+
+}  // namespace fp4q

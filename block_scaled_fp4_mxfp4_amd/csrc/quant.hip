@@ -1,0 +1,534 @@
+// quant.hip -- memory-bound quantization kernels of libfp4q for gfx950:
+// tensor amax, NVFP4 and MXFP4 block quantization (with the fused balance
+// scale and block-32 Hadamard rotation), the standalone rotation, the
+// balance-scale calibration statistic and first-order Sigma-Delta
+// re-quantization.
+//
+// Work mapping shared by the block kernels: one lane owns 8 consecutive
+// elements of a row (one 16-byte load of bf16, two of fp32), so a wavefront
+// reads 1 KiB (bf16) of contiguous memory per load instruction and writes
+// its packed codes as one contiguous 256-byte store.  An NVFP4 16-block is
+// spread over a lane pair, an MXFP4 32-block over a lane quad; the block
+// maximum and the Hadamard butterflies between lanes use DPP quad
+// permutations, so no LDS is touched.
+//
+// The arithmetic order follows the recipes stated in include/fp4q.h; each
+// step is one binary32 operation (-ffp-contract=off, IEEE division).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.h"
+#include "internal.h"
+
+namespace fp4q {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------- helpers ----
+
+__device__ __forceinline__ float dpp_xor1(float v) {   // quad_perm [1,0,3,2]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {   // quad_perm [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float v[8]) {
+  if constexpr (BF16) {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ uint32_t pack8(const uint32_t c[8]) {
+  uint32_t p = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p |= (c[i] & 0xFu) << (4 * i);
+  return p;
+}
+
+// Tensor-scale cell encoding while a dynamic quantization is in flight:
+// bit 31 set -> the low 31 bits are max|x| (non-negative binary32) and
+// s_t = fl(A / 1536); bit 31 clear -> the cell already holds s_t.
+constexpr uint32_t kAmaxFlag = 0x80000000u;
+
+__device__ __forceinline__ float read_tensor_scale(const float* cell, int dynamic) {
+  const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cell));
+  if (dynamic && (u & kAmaxFlag)) return __uint_as_float(u & 0x7FFFFFFFu) / 1536.0f;
+  return __uint_as_float(u);
+}
+
+// Element offset of chunk c (8 elements) in a [rows][ld] tensor whose rows
+// hold cpr = cols/8 chunks.
+template <bool CONTIG>
+__device__ __forceinline__ int64_t chunk_offset(int64_t c, int64_t cpr, int64_t ld) {
+  if constexpr (CONTIG) return c * 8;
+  const int64_t r = c / cpr;
+  return r * ld + (c - r * cpr) * 8;
+}
+
+// ---------------------------------------------------------------- amax ----
+
+__global__ void k_cell_reset(uint32_t* cell) { *cell = kAmaxFlag; }
+
+template <bool BF16, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t nchunks,
+                                                   int64_t cpr, int64_t ld,
+                                                   uint32_t* __restrict__ cell) {
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
+    float v[8];
+    load8<BF16>(x, chunk_offset<CONTIG>(c, cpr, ld), v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+  }
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, red[i]);
+    atomicMax(cell, kAmaxFlag | __float_as_uint(m));
+  }
+}
+
+// -------------------------------------------------------------- NVFP4 ----
+
+constexpr int kNvUnroll = 4;
+
+template <bool BF16, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
+    const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* ts, int dynamic) {
+  const float st = read_tensor_scale(ts, dynamic);
+  const float six_st = 6.0f * st;
+  float v[kNvUnroll][8];
+  int64_t cidx[kNvUnroll];
+#pragma unroll
+  for (int u = 0; u < kNvUnroll; ++u) {
+    cidx[u] = ((int64_t)blockIdx.x * kNvUnroll + u) * kThreads + threadIdx.x;
+    if (cidx[u] < nchunks) {
+      load8<BF16>(x, chunk_offset<CONTIG>(cidx[u], cpr, ld), v[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kNvUnroll; ++u) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[u][i]));
+    a = fmaxf(a, dpp_xor1(a));                       // block max over the lane pair
+    uint32_t sb = 0;
+    if (a > 0.0f && st > 0.0f) sb = e4m3_ceil(a / six_st);
+    const float s = st * e4m3_decode(sb);
+    const float rho = 1.0f / s;
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = (s == 0.0f) ? 0u : e2m1_encode(v[u][i] * rho);
+    if (cidx[u] < nchunks) {
+      codes[cidx[u]] = pack8(c);
+      if (!(cidx[u] & 1)) scales[cidx[u] >> 1] = (uint8_t)sb;
+    }
+  }
+  if (dynamic && blockIdx.x == 0 && threadIdx.x == 0) *ts = st;
+}
+
+// -------------------------------------------------------------- MXFP4 ----
+
+// Per-lane part of the block-32 transform: z = x * t; stages h = 1, 2, 4
+// inside the lane; h = 8 and h = 16 across the quad (lane bit 0 and bit 1);
+// then times fl32(1/sqrt(32)).  The lower partner of every butterfly gets
+// a + b, the upper one a - b, with a the lower element -- the same IEEE
+// operations on the same operands as the sequential definition.
+__device__ __forceinline__ void hadamard32_lane(float z[8], int qlane) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = z[i], b = z[i + h];
+      z[i] = a + b;
+      z[i + h] = a - b;
+    }
+  }
+  const bool up1 = qlane & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = dpp_xor1(z[i]);
+    z[i] = up1 ? (o - z[i]) : (z[i] + o);
+  }
+  const bool up2 = qlane & 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = dpp_xor2(z[i]);
+    z[i] = up2 ? (o - z[i]) : (z[i] + o);
+  }
+  const float c = 0.17677669529663687f;   // fl32(1/sqrt(32)) = 0x3E3504F3
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = z[i] * c;
+}
+
+__device__ __forceinline__ void apply_chan_scale(float z[8], const float* __restrict__ t,
+                                                 int64_t col) {
+  const float4* p = reinterpret_cast<const float4*>(t + col);
+  const float4 a = p[0], b = p[1];
+  z[0] = z[0] * a.x; z[1] = z[1] * a.y; z[2] = z[2] * a.z; z[3] = z[3] * a.w;
+  z[4] = z[4] * b.x; z[5] = z[5] * b.y; z[6] = z[6] * b.z; z[7] = z[7] * b.w;
+}
+
+constexpr int kMxUnroll = 2;
+
+template <bool BF16, bool CONTIG, bool SCALE, bool HAD>
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
+    const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
+    const float* __restrict__ t, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  float v[kMxUnroll][8];
+  int64_t cidx[kMxUnroll];
+#pragma unroll
+  for (int u = 0; u < kMxUnroll; ++u) {
+    cidx[u] = ((int64_t)blockIdx.x * kMxUnroll + u) * kThreads + threadIdx.x;
+    if (cidx[u] < nchunks) {
+      load8<BF16>(x, chunk_offset<CONTIG>(cidx[u], cpr, ld), v[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    }
+  }
+  const int qlane = threadIdx.x & 3;
+#pragma unroll
+  for (int u = 0; u < kMxUnroll; ++u) {
+    if constexpr (SCALE) {
+      const int64_t c = cidx[u] < nchunks ? cidx[u] : 0;
+      apply_chan_scale(v[u], t, (c % cpr) * 8);
+    }
+    if constexpr (HAD) hadamard32_lane(v[u], qlane);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[u][i]));
+    a = fmaxf(a, dpp_xor1(a));
+    a = fmaxf(a, dpp_xor2(a));
+    const bool zero = !(a > 0.0f);
+    const int32_t e = zero ? -127 : mx_block_exponent(a);
+    const float inv = pow2_neg(e);
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = zero ? 0u : e2m1_encode(v[u][i] * inv);
+    if (cidx[u] < nchunks) {
+      codes[cidx[u]] = pack8(c);
+      if (qlane == 0) scales[cidx[u] >> 2] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+template <bool BF16, bool CONTIG, bool SCALE>
+__global__ __launch_bounds__(kThreads) void k_hadamard32(
+    const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
+    const float* __restrict__ t, float* __restrict__ y, int64_t ldy) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float v[8];
+  if (c < nchunks) {
+    load8<BF16>(x, chunk_offset<CONTIG>(c, cpr, ld), v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  if constexpr (SCALE) apply_chan_scale(v, t, ((c < nchunks ? c : 0) % cpr) * 8);
+  hadamard32_lane(v, threadIdx.x & 3);
+  if (c < nchunks) {
+    const int64_t r = c / cpr;
+    float4* p = reinterpret_cast<float4*>(y + r * ldy + (c - r * cpr) * 8);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// ------------------------------------------------------ balance scale ----
+
+// One workgroup per 64 columns: 4 row-lanes x 64 column-lanes; fp64 column
+// sums, two passes for the standard deviation (mean first).
+template <bool BF16>
+__device__ __forceinline__ double load1(const void* p, int64_t off) {
+  if constexpr (BF16) return (double)bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[off]);
+  return (double)reinterpret_cast<const float*>(p)[off];
+}
+
+template <bool WBF16, bool XBF16>
+__global__ __launch_bounds__(kThreads) void k_balance(const void* __restrict__ w, int64_t N,
+                                                      int64_t K, int64_t ldw,
+                                                      const void* __restrict__ x, int64_t M,
+                                                      int64_t ldx, double alpha,
+                                                      float* __restrict__ t_out,
+                                                      float* __restrict__ u_out) {
+  __shared__ double red[4][64];
+  const int cl = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 64 + cl;
+  const bool ok = col < K;
+  // pass 1: column mean of W
+  double s = 0.0;
+  if (ok)
+    for (int64_t r = rl; r < N; r += 4) s += load1<WBF16>(w, r * ldw + col);
+  red[rl][cl] = s;
+  __syncthreads();
+  const double mean = (red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl]) / (double)N;
+  __syncthreads();
+  // pass 2: sum of squared deviations
+  s = 0.0;
+  if (ok)
+    for (int64_t r = rl; r < N; r += 4) {
+      const double d = load1<WBF16>(w, r * ldw + col) - mean;
+      s += d * d;
+    }
+  red[rl][cl] = s;
+  __syncthreads();
+  const double var = (red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl]) / (double)N;
+  __syncthreads();
+  // activation column mean square
+  s = 0.0;
+  if (ok)
+    for (int64_t r = rl; r < M; r += 4) {
+      const double v = load1<XBF16>(x, r * ldx + col);
+      s += v * v;
+    }
+  red[rl][cl] = s;
+  __syncthreads();
+  if (rl == 0 && ok) {
+    const double ms = (red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl]) / (double)M;
+    const double sigma = fmax(sqrt(var), 1e-12);
+    const double rms = fmax(sqrt(ms), 1e-12);
+    double tt = pow(sigma, alpha) / pow(rms, 1.0 - alpha);
+    tt = fmin(fmax(tt, 0x1p-16), 0x1p16);
+    t_out[col] = (float)tt;
+    u_out[col] = (float)(1.0 / tt);
+  }
+}
+
+// -------------------------------------------------------- Sigma-Delta ----
+
+constexpr int kSdMaxSeg = 16;
+
+struct SdArgs {
+  const float* w[kSdMaxSeg];
+  const uint8_t* scales[kSdMaxSeg];
+  const float* ts[kSdMaxSeg];
+  float* res[kSdMaxSeg];
+  uint8_t* codes[kSdMaxSeg];
+  int64_t nchunks[kSdMaxSeg];
+  int32_t wg_start[kSdMaxSeg + 1];
+  int32_t nseg;
+};
+
+constexpr int kSdUnroll = 2;
+
+__global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int steps,
+                                                          int64_t bank_stride) {
+  int seg = 0;
+  while (seg + 1 < args.nseg && (int)blockIdx.x >= args.wg_start[seg + 1]) ++seg;
+  const int64_t wg = (int64_t)blockIdx.x - args.wg_start[seg];
+  const int64_t n = args.nchunks[seg];
+  const float st = *args.ts[seg];
+  const float* __restrict__ w = args.w[seg];
+  float* __restrict__ res = args.res[seg];
+  float x[kSdUnroll][8], r[kSdUnroll][8];
+  int64_t cidx[kSdUnroll];
+#pragma unroll
+  for (int u = 0; u < kSdUnroll; ++u) {
+    cidx[u] = (wg * kSdUnroll + u) * kThreads + threadIdx.x;
+    const bool in = cidx[u] < n;
+    if (in) {
+      load8<false>(w, cidx[u] * 8, x[u]);
+      load8<false>(res, cidx[u] * 8, r[u]);
+    }
+    const uint32_t sb = in ? args.scales[seg][cidx[u] >> 1] : 0u;
+    const float s = st * e4m3_decode(sb);
+    const float rho = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float xi = in ? x[u][i] * rho : 0.0f;
+      if (!(s != 0.0f)) xi = 0.0f;
+      xi = fminf(fmaxf(xi, -6.0f), 6.0f);
+      x[u][i] = xi;
+      if (!in) r[u][i] = 0.0f;
+    }
+  }
+  uint8_t* codes = args.codes[seg];
+  for (int k = 0; k < steps; ++k) {
+#pragma unroll
+    for (int u = 0; u < kSdUnroll; ++u) {
+      uint32_t c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = x[u][i] + r[u][i];
+        c[i] = e2m1_encode(v);
+        r[u][i] = v - e2m1_decode(c[i]);
+      }
+      if (cidx[u] < n)
+        reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pack8(c);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kSdUnroll; ++u) {
+    if (cidx[u] < n) {
+      float4* p = reinterpret_cast<float4*>(res + cidx[u] * 8);
+      p[0] = make_float4(r[u][0], r[u][1], r[u][2], r[u][3]);
+      p[1] = make_float4(r[u][4], r[u][5], r[u][6], r[u][7]);
+    }
+  }
+}
+
+inline unsigned grid_for(int64_t items, int64_t per_block) {
+  return (unsigned)((items + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers ----
+
+hipError_t launch_amax_to_cell(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
+                               float* cell, hipStream_t s) {
+  const int64_t cpr = cols / 8, n = rows * cpr;
+  const bool contig = (ldx == cols);
+  hipLaunchKernelGGL(k_cell_reset, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(cell));
+  int64_t g = grid_for(n, kThreads * 8);
+  if (g > 2048) g = 2048;
+  if (g < 1) g = 1;
+  auto* u = reinterpret_cast<uint32_t*>(cell);
+  if (bf16) {
+    if (contig) hipLaunchKernelGGL((k_amax<true, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
+    else hipLaunchKernelGGL((k_amax<true, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
+  } else {
+    if (contig) hipLaunchKernelGGL((k_amax<false, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
+    else hipLaunchKernelGGL((k_amax<false, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
+                              hipStream_t s) {
+  const int dynamic = !ts_is_input;
+  if (dynamic) {
+    hipError_t e = launch_amax_to_cell(x, bf16, rows, cols, ldx, ts, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t cpr = cols / 8, n = rows * cpr;
+  const bool contig = (ldx == cols);
+  const unsigned g = grid_for(n, (int64_t)kThreads * kNvUnroll);
+  auto* c32 = reinterpret_cast<uint32_t*>(codes);
+  if (bf16) {
+    if (contig) hipLaunchKernelGGL((k_quant_nvfp4<true, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+    else hipLaunchKernelGGL((k_quant_nvfp4<true, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+  } else {
+    if (contig) hipLaunchKernelGGL((k_quant_nvfp4<false, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+    else hipLaunchKernelGGL((k_quant_nvfp4<false, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+template <bool BF16, bool CONTIG>
+void launch_mx_variant(bool scale, bool had, unsigned g, hipStream_t s, const void* x, int64_t n,
+                       int64_t cpr, int64_t ld, const float* t, uint32_t* c, uint8_t* sc) {
+  if (scale && had) hipLaunchKernelGGL((k_quant_mxfp4<BF16, CONTIG, true, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ld, t, c, sc);
+  else if (scale) hipLaunchKernelGGL((k_quant_mxfp4<BF16, CONTIG, true, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ld, t, c, sc);
+  else if (had) hipLaunchKernelGGL((k_quant_mxfp4<BF16, CONTIG, false, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ld, t, c, sc);
+  else hipLaunchKernelGGL((k_quant_mxfp4<BF16, CONTIG, false, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ld, t, c, sc);
+}
+template <bool BF16, bool CONTIG>
+void launch_had_variant(bool scale, unsigned g, hipStream_t s, const void* x, int64_t n,
+                        int64_t cpr, int64_t ld, const float* t, float* y, int64_t ldy) {
+  if (scale) hipLaunchKernelGGL((k_hadamard32<BF16, CONTIG, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ld, t, y, ldy);
+  else hipLaunchKernelGGL((k_hadamard32<BF16, CONTIG, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ld, t, y, ldy);
+}
+}  // namespace
+
+hipError_t launch_quant_mxfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
+                              const float* chan_scale, int hadamard, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const int64_t cpr = cols / 8, n = rows * cpr;
+  const bool contig = (ldx == cols);
+  const unsigned g = grid_for(n, (int64_t)kThreads * kMxUnroll);
+  auto* c32 = reinterpret_cast<uint32_t*>(codes);
+  const bool sc = chan_scale != nullptr, had = hadamard != 0;
+  if (bf16) {
+    if (contig) launch_mx_variant<true, true>(sc, had, g, s, x, n, cpr, ldx, chan_scale, c32, scales);
+    else launch_mx_variant<true, false>(sc, had, g, s, x, n, cpr, ldx, chan_scale, c32, scales);
+  } else {
+    if (contig) launch_mx_variant<false, true>(sc, had, g, s, x, n, cpr, ldx, chan_scale, c32, scales);
+    else launch_mx_variant<false, false>(sc, had, g, s, x, n, cpr, ldx, chan_scale, c32, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard32_scale(const void* x, int bf16, int64_t rows, int64_t cols,
+                                   int64_t ldx, const float* chan_scale, float* y, int64_t ldy,
+                                   hipStream_t s) {
+  const int64_t cpr = cols / 8, n = rows * cpr;
+  const bool contig = (ldx == cols);
+  const unsigned g = grid_for(n, kThreads);
+  const bool sc = chan_scale != nullptr;
+  if (bf16) {
+    if (contig) launch_had_variant<true, true>(sc, g, s, x, n, cpr, ldx, chan_scale, y, ldy);
+    else launch_had_variant<true, false>(sc, g, s, x, n, cpr, ldx, chan_scale, y, ldy);
+  } else {
+    if (contig) launch_had_variant<false, true>(sc, g, s, x, n, cpr, ldx, chan_scale, y, ldy);
+    else launch_had_variant<false, false>(sc, g, s, x, n, cpr, ldx, chan_scale, y, ldy);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K, int64_t ldw,
+                                const void* x, int x_bf16, int64_t M, int64_t ldx, double alpha,
+                                float* t_out, float* u_out, hipStream_t s) {
+  const unsigned g = grid_for(K, 64);
+  if (w_bf16 && x_bf16) hipLaunchKernelGGL((k_balance<true, true>), dim3(g), dim3(kThreads), 0, s, w, N, K, ldw, x, M, ldx, alpha, t_out, u_out);
+  else if (w_bf16) hipLaunchKernelGGL((k_balance<true, false>), dim3(g), dim3(kThreads), 0, s, w, N, K, ldw, x, M, ldx, alpha, t_out, u_out);
+  else if (x_bf16) hipLaunchKernelGGL((k_balance<false, true>), dim3(g), dim3(kThreads), 0, s, w, N, K, ldw, x, M, ldx, alpha, t_out, u_out);
+  else hipLaunchKernelGGL((k_balance<false, false>), dim3(g), dim3(kThreads), 0, s, w, N, K, ldw, x, M, ldx, alpha, t_out, u_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
+                              int64_t bank_stride, hipStream_t s) {
+  for (int base = 0; base < nseg; base += kSdMaxSeg) {
+    SdArgs a = {};
+    const int cnt = (nseg - base) < kSdMaxSeg ? (nseg - base) : kSdMaxSeg;
+    a.nseg = cnt;
+    int32_t wg = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const fp4q_sd_segment& g = segs[base + i];
+      a.w[i] = g.w;
+      a.scales[i] = g.scales;
+      a.ts[i] = g.tensor_scale;
+      a.res[i] = g.residue;
+      a.codes[i] = g.codes;
+      a.nchunks[i] = g.rows * (g.cols / 8);
+      a.wg_start[i] = wg;
+      wg += (int32_t)grid_for(a.nchunks[i], (int64_t)kThreads * kSdUnroll);
+    }
+    a.wg_start[cnt] = wg;
+    hipLaunchKernelGGL(k_sigma_delta, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace fp4q

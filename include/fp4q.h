@@ -1,0 +1,226 @@
+/*
+ * fp4q.h -- C ABI of libfp4q: block-scaled 4-bit (NVFP4 / MXFP4) W4A4 linear
+ * layer and looped Sigma-Delta weight re-quantization on AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * Sources (page titles; the section, box or step that defines each call is
+ * named at the call):
+ *   [LQ]   "Looped Transformer quantization: error propagation, NVFP4 and
+ *          Sigma-Delta modulation" (mer.dev, loopquant-fp4)
+ *   [GDN]  "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the
+ *          Recurrent Half of a Hybrid 27B LLM" (paper 2609.04098)
+ *   [MQ]   "MACaQ: Fast, Model Agnostic Calibrated Quantization for
+ *          Low-Precision Weights and Activations" (paper 2611.10649)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every data pointer is a DEVICE pointer (memory of the current HIP
+ *    device) unless the comment says "host".  `stream` is a hipStream_t
+ *    passed as void* (NULL = the default stream).
+ *  - The caller owns and allocates every buffer; the library never
+ *    allocates, frees or synchronizes.  Every call validates its arguments
+ *    on the host, then enqueues its kernels on `stream` and returns; results
+ *    are valid once the stream has reached that point.
+ *  - Matrices are row-major with the reduction / block axis (cols, K)
+ *    contiguous.  `ld*` arguments are row strides in ELEMENTS of the input
+ *    type.  Outputs written by the library are dense: packed codes are
+ *    [rows][cols/2] bytes, element 2j in the low nibble of byte j and
+ *    element 2j+1 in the high nibble; NVFP4 block scales are [rows][cols/16]
+ *    E4M3 bytes; MXFP4 block scales are [rows][cols/32] E8M0 bytes.
+ *  - Weights are stored [N][K] (out features x in features); GEMMs compute
+ *    Y[M][N] = A[M][K] * B[N][K]^T with fp32 accumulation and fp32 output.
+ *  - Non-finite inputs are outside the contract (results unspecified, no
+ *    fault).
+ *  - Return value: FP4Q_OK or an error status; on error nothing was
+ *    enqueued.  fp4q_last_error() returns a thread-local description of the
+ *    most recent failure on the calling thread.
+ *  - Calls on the same stream are ordered; calls that share output buffers
+ *    on different streams race.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+enum fp4q_status {
+  FP4Q_OK = 0,
+  FP4Q_ERR_NULL_PTR = 1,    /* a required pointer is NULL                         */
+  FP4Q_ERR_BAD_SHAPE = 2,   /* sizes <= 0, cols not a multiple of the block, ld < cols, ... */
+  FP4Q_ERR_BAD_ALIGN = 3,   /* a pointer or row stride breaks the 16-byte alignment rule */
+  FP4Q_ERR_BAD_DTYPE = 4,   /* unknown element type / format enum                  */
+  FP4Q_ERR_BAD_ARG = 5,     /* any other invalid argument                          */
+  FP4Q_ERR_DEVICE = 6,      /* current device is not gfx950, or no device          */
+  FP4Q_ERR_LAUNCH = 7       /* the HIP runtime rejected a launch                   */
+};
+
+enum fp4q_dtype { FP4Q_F32 = 0, FP4Q_BF16 = 1 };
+enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 };
+
+/* ABI version of the loaded library (FP4Q_ABI_VERSION at build time). */
+int fp4q_abi_version(void);
+/* Static name of a status code. */
+const char* fp4q_status_str(int status);
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* fp4q_last_error(void);
+
+/*
+ * NVFP4 quantization.  [LQ] section 0.2 (E2M1 elements, 16-element blocks,
+ * E4M3 block scale, FP32 tensor scale) and section 2.2 (default tensor scale
+ * max|W|/(6*256); the candidate E4M3 block scale is rounded up); [GDN]
+ * background box "NVFP4 and W4A4" (block scale = block max / 6).
+ * Arithmetic, every step one IEEE binary32 operation (round to nearest even):
+ *     s_t = A / 1536 with A = max|x| (or the caller's s_t)
+ *     s_b = ceil_E4M3(a_b / (6 * s_t)),  a_b = max|x| of the block
+ *     rho = 1 / (s_t * s_b);  code = nearest E2M1 of x * rho (ties to even
+ *     mantissa, saturating at +-6, sign bit = sign of x * rho)
+ *   A block with a_b == 0, or a tensor with s_t == 0, gets scale 0 and codes 0.
+ * x:       [rows][ldx] elements of type x_dtype (FP4Q_F32 or FP4Q_BF16);
+ *          16-byte aligned, ldx*sizeof(elem) a multiple of 16, ldx >= cols.
+ * cols:    multiple of 16.
+ * codes:   [rows][cols/2] bytes, 16-byte aligned (output).
+ * scales:  [rows][cols/16] E4M3 bytes (output).
+ * tensor_scale: one fp32.  tensor_scale_is_input == 0: the library computes
+ *          A over the whole tensor on the stream and writes s_t here (the
+ *          location is also used as the reduction cell while the call runs);
+ *          == 1: s_t is read from here (must be finite and >= +0).
+ */
+int fp4q_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                        int tensor_scale_is_input, void* stream);
+
+/*
+ * MXFP4 quantization with the optional online transform.  [MQ] background
+ * box "MXFP4 micro-scaling format" (OCP MXFP4: 32-element blocks, E8M0
+ * power-of-two scale, E2M1 elements) and "Method steps" 1-3 (activations
+ * times the per-channel balance scale t, then the block-32 Hadamard
+ * rotation; scaling before rotation; exponent derived from the block max).
+ * Arithmetic (binary32, one operation at a time):
+ *     z = x * chan_scale[col]                    (skipped if chan_scale == NULL)
+ *     z' = FWHT32(z) in Sylvester order, stages h = 1,2,4,8,16, then times
+ *          fl32(1/sqrt(32))                      (only if hadamard32 == 1)
+ *     e = floor(log2 max|z'| over the block) - 2, clamped to [-127, 127];
+ *     byte = e + 127 (0 for an all-zero block); code = nearest E2M1 of z'*2^-e
+ * x:          as for fp4q_quantize_nvfp4; cols a multiple of 32.
+ * chan_scale: [cols] fp32 or NULL.
+ * codes:      [rows][cols/2] (output, 16-byte aligned).
+ * scales:     [rows][cols/32] E8M0 bytes (output).
+ */
+int fp4q_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        const float* chan_scale, int hadamard32,
+                        uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Standalone balance scale + block-32 Hadamard rotation to fp32, the
+ * weight-side transform W' = (W / t) B of [MQ] "Method steps" step 2 (pass
+ * chan_scale = 1/t).  Same arithmetic as the transform inside
+ * fp4q_quantize_mxfp4, so quantizing y with hadamard32 = 0 gives the same
+ * codes as the fused call.
+ * y: [rows][ldy] fp32 output, 16-byte aligned, ldy >= cols, ldy % 4 == 0.
+ */
+int fp4q_hadamard32_scale(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                          const float* chan_scale, float* y, int64_t ldy, void* stream);
+
+/*
+ * Per-channel balance scale (calibration statistic; [MQ] "Core method" step
+ * (i)): t_j = sigma_j^alpha / rms_j^(1-alpha), sigma_j the population
+ * standard deviation of column j of W [N][K], rms_j the root mean square of
+ * column j of the calibration activations X [M][K]; each factor floored at
+ * 1e-12, t clamped to [2^-16, 2^16]; computed in fp64 on the device.
+ * Writes t_out[j] = fl32(t_j) (activation side) and u_out[j] = fl32(1/t_j)
+ * (weight side).  w, x: bf16 or fp32, row strides ldw, ldx (elements).
+ */
+int fp4q_balance_scale(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                       const void* x, int x_dtype, int64_t M, int64_t ldx,
+                       double alpha, float* t_out, float* u_out, void* stream);
+
+/*
+ * One linear of the looped core for first-order Sigma-Delta re-quantization.
+ * The ARRAY of segments lives in HOST memory; the pointers inside it are
+ * device pointers.
+ *   w:            [rows][cols] fp32 master weight (dense)
+ *   scales:       [rows][cols/16] E4M3 block scales and
+ *   tensor_scale: one fp32 s_t -- the FIXED NVFP4 scale of this weight,
+ *                 e.g. from fp4q_quantize_nvfp4(w, ...)
+ *   residue:      [rows][cols] fp32 Sigma-Delta state r, read and written;
+ *                 the caller zeroes it before the first step of a forward
+ *   codes:        output code bank(s), [rows][cols/2] bytes each, 16-byte aligned
+ */
+typedef struct fp4q_sd_segment {
+  const float* w;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  float* residue;
+  uint8_t* codes;
+  int64_t rows;
+  int64_t cols;
+} fp4q_sd_segment;
+
+/*
+ * First-order Sigma-Delta re-quantization over nseg weights in one launch.
+ * [LQ] section 2.1 (fixed scale s, r_0 = 0, v_k = x + r_{k-1},
+ * q_k = Q(v_k), r_k = v_k - q_k), section 2.2 (saturating nearest quantizer,
+ * x inside the hull [-6, 6]) and the STE listing of section 2.5 (x = W / s,
+ * q = nearest E2M1 code, r zeroed every forward).
+ * Per element, binary32:  x = clamp(w * rho, -6, 6) with rho = 1/(s_t*s_b)
+ * (0 in a zero-scale block);  for each step: v = x + r; code = nearest E2M1
+ * of v; r = v - value(code) (exact).
+ * steps >= 1 consecutive steps are run with r kept on chip; step j writes its
+ * codes at segs[i].codes + j * bank_stride_bytes (bank_stride_bytes is
+ * ignored when steps == 1 and otherwise must be >= rows*cols/2 and a
+ * multiple of 16).  r is written back once, after the last step.
+ * nseg in [1, 64]; every segment: rows >= 1, cols a multiple of 16.
+ */
+int fp4q_sigma_delta_requant(const fp4q_sd_segment* segs, int nseg, int steps,
+                             int64_t bank_stride_bytes, void* stream);
+
+/*
+ * W4A4 GEMM over quantized operands: Y = dequant(A) * dequant(B)^T, fp32
+ * accumulate, fp32 out.  [MQ] "Core method" (y = [(x*t)B]_MXFP4 W'^T_MXFP4)
+ * and [GDN] "NVFP4 and W4A4" (both operands NVFP4, GEMM on the 4-bit data).
+ * fmt == FP4Q_MXFP4: a_scales [M][K/32], b_scales [N][K/32] E8M0;
+ *                    a_tscale, b_tscale ignored (may be NULL).
+ * fmt == FP4Q_NVFP4: a_scales [M][K/16], b_scales [N][K/16] E4M3;
+ *                    a_tscale, b_tscale point to one fp32 each.
+ * a_codes [M][K/2], b_codes [N][K/2] (16-byte aligned); scales 8-byte
+ * aligned; K a multiple of 128; y [M][ldy] fp32 (4-byte aligned), ldy >= N.
+ */
+int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
+                   const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
+                   int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream);
+
+/*
+ * W4A16 GEMM: Y = A_bf16 * dequant(B_nvfp4)^T, fp32 accumulate and output.
+ * The matrix product the looped core runs on each step's re-quantized weight
+ * ([LQ] section 4: the core-linear microbenchmark with online NVFP4 codes).
+ * a: [M][lda] bf16, 16-byte aligned, lda % 8 == 0.  B as for NVFP4 above.
+ * K a multiple of 128.
+ */
+int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda,
+                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
+                    int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream);
+
+/*
+ * Decode-shaped NVFP4 W4A4 linear with the activation quantization fused
+ * into the GEMM ([GDN] "Limitations": decode was slowed by the small-batch
+ * NVFP4 activation-quantization kernel).  Quantizes A (bf16) exactly as
+ * fp4q_quantize_nvfp4 does and multiplies by the NVFP4 weight B;
+ * Y is bit-identical to fp4q_quantize_nvfp4 followed by fp4q_gemm_w4a4.
+ * M in [1, 16]; K a multiple of 128 and at most 7168 (A is held on chip).
+ * a_tscale: one fp32, same in/out rule as fp4q_quantize_nvfp4's
+ * tensor_scale.
+ */
+int fp4q_linear_w4a4(const void* a_bf16, int64_t lda, float* a_tscale, int a_tscale_is_input,
+                     const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
+                     int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

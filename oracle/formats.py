@@ -147,12 +147,13 @@ def e4m3_ceil(y: np.ndarray) -> np.ndarray:
 
     The NVFP4 block scale is "rounded up" to E4M3 (loopquant page, section
     2.2, the paragraph applying the bound to the signed E2M1 code book).
-    Values above 448 saturate to 448 (byte 0x7E); y == 0 gives 0.
+    Values above 448 (including +inf) saturate to 448 (byte 0x7E); y == 0
+    gives 0.
     Brute force over the 127 non-negative finite codes 0x00..0x7E, which are
     in increasing order of value.
     """
     y = np.asarray(y, dtype=np.float64)
-    assert np.all(np.isfinite(y)) and np.all(y >= 0)
+    assert not np.any(np.isnan(y)) and np.all(y >= 0)
     table = E4M3_VALUES[:127]                      # 0x00 .. 0x7E, increasing
     assert np.all(np.diff(table) > 0)
     idx = np.searchsorted(table, y, side="left")   # first table[i] >= y

@@ -51,7 +51,7 @@ def block_scales(x: np.ndarray, s_t) -> np.ndarray:
     s_t = F32(s_t)
     a_b = np.abs(x).reshape(R, K // BLOCK, BLOCK).max(axis=-1)       # exact
     six_st = F32(F32(6.0) * s_t)
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         y = (a_b / six_st).astype(F32)                                # fl32 division
     y = np.where((a_b == 0) | (s_t == 0), F32(0), y)
     return e4m3_ceil(y.astype(np.float64))

@@ -74,12 +74,14 @@ def sigma_delta_exact(x: Fraction, quantizer: Callable[[Fraction], Fraction],
     return qs, rs
 
 
-def normalised_weight(w: np.ndarray):
+def normalised_weight(w: np.ndarray, tensor_scale=None):
     """Fixed-scale setup of the NVFP4 chain for an fp32 master ``w`` [R, K]:
-    returns (x float32 [R, K], scale bytes, s_t, block_zero mask [R, K])."""
+    returns (x float32 [R, K], scale bytes, s_t, block_zero mask [R, K]).
+    ``tensor_scale`` (the s_t of the whole weight) lets a caller run the
+    chain on a subset of rows of a larger weight."""
     w = np.asarray(w, dtype=F32)
     R, K = w.shape
-    _, sb_bytes, s_t = nvfp4.quantize(w)
+    _, sb_bytes, s_t = nvfp4.quantize(w, tensor_scale=tensor_scale)
     s_b = e4m3_decode(sb_bytes).astype(F32)
     s = (s_t * s_b).astype(F32)
     with np.errstate(divide="ignore"):
@@ -91,15 +93,16 @@ def normalised_weight(w: np.ndarray):
     return x, sb_bytes, s_t, zero
 
 
-def sigma_delta_nvfp4(w: np.ndarray, steps: int, r0: np.ndarray = None):
+def sigma_delta_nvfp4(w: np.ndarray, steps: int, r0: np.ndarray = None, tensor_scale=None):
     """Run ``steps`` Sigma-Delta accesses on the fp32 master ``w`` [R, K].
 
     Returns a dict with ``codes`` (list of uint8 [R, K] per step, unpacked),
     ``residues`` (list of float32 [R, K] after each step), ``scales``
     (E4M3 bytes [R, K/16]) and ``s_t``.  ``r0`` (float32) continues a chain
-    from a saved residue; default zeros.
+    from a saved residue; default zeros.  ``tensor_scale`` as in
+    :func:`normalised_weight`.
     """
-    x, sb_bytes, s_t, zero = normalised_weight(w)
+    x, sb_bytes, s_t, zero = normalised_weight(w, tensor_scale)
     r = np.zeros_like(x) if r0 is None else np.asarray(r0, dtype=F32).copy()
     codes_all, res_all = [], []
     for _ in range(steps):

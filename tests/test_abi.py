@@ -1,0 +1,83 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry
+point include/fp4q.h declares, and rejects invalid arguments with the
+documented status codes before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+LIB = os.path.join(ROOT, "block_scaled_fp4_mxfp4_amd", "libfp4q.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def fp4q():
+    if not os.path.exists(LIB):
+        pytest.skip("libfp4q.so not built")
+    from block_scaled_fp4_mxfp4_amd import fp4q as m
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_hadamard32_scale",
+              "fp4q_sigma_delta_requant", "fp4q_gemm_w4a4", "fp4q_gemm_w4a16", "fp4q_linear_w4a4",
+              "fp4q_balance_scale", "fp4q_abi_version", "fp4q_status_str", "fp4q_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fp4q):
+    lib = ctypes.CDLL(LIB)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(fp4q.EXPORTED)
+    assert fp4q.abi_version() == 1
+    assert fp4q.lib.fp4q_status_str(2) == b"FP4Q_ERR_BAD_SHAPE"
+
+
+def test_validation_happens_before_any_device_work(fp4q):
+    L = fp4q.lib
+    P = ctypes.c_void_p
+    fake = P(0x1000)          # never dereferenced: validation fails first
+    fake16 = P(0x10000)
+    assert L.fp4q_quantize_nvfp4(None, 1, 4, 32, 32, fake16, fake, fake, 0, None) == 1
+    assert b"NULL" in L.fp4q_last_error()
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 24, 24, fake16, fake, fake, 0, None) == 2      # cols % 16
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 16, fake16, fake, fake, 0, None) == 2      # ld < cols
+    assert L.fp4q_quantize_nvfp4(P(0x1002), 1, 4, 32, 32, fake16, fake, fake, 0, None) == 3   # misaligned x
+    assert L.fp4q_quantize_nvfp4(fake16, 7, 4, 32, 32, fake16, fake, fake, 0, None) == 4      # dtype
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, fake, fake, 2, None) == 5      # flag
+    assert L.fp4q_quantize_mxfp4(fake16, 1, 4, 48, 48, None, 0, fake16, fake, None) == 2      # cols % 32
+    assert L.fp4q_quantize_mxfp4(fake16, 1, 4, 64, 64, None, 3, fake16, fake, None) == 5
+    assert L.fp4q_gemm_w4a4(5, fake16, fake16, fake, fake16, fake16, fake, 4, 4, 128, fake16, 4, None) == 4
+    assert L.fp4q_gemm_w4a4(0, fake16, fake16, None, fake16, fake16, fake, 4, 4, 128, fake16, 4, None) == 1
+    assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, 4, 4, 96, fake16, 4, None) == 2
+    assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, 4, 8, 128, fake16, 4, None) == 2
+    assert L.fp4q_linear_w4a4(fake16, 128, fake, 0, fake16, fake16, fake, 17, 8, 128, fake16, 8, None) == 2
+    assert L.fp4q_linear_w4a4(fake16, 8192, fake, 0, fake16, fake16, fake, 1, 8, 8192, fake16, 8, None) == 2
+    assert L.fp4q_gemm_w4a16(fake16, 100, fake16, fake16, fake, 4, 4, 128, fake16, 4, None) == 2
+    seg = fp4q.SdSegment(0x10000, 0x1000, 0x1000, 0x10000, 0x10000, 4, 20)
+    arr = (fp4q.SdSegment * 1)(seg)
+    assert L.fp4q_sigma_delta_requant(arr, 1, 1, 0, None) == 2                               # cols % 16
+    assert L.fp4q_sigma_delta_requant(arr, 0, 1, 0, None) == 5
+    seg2 = fp4q.SdSegment(0x10000, 0x1000, 0x1000, 0x10000, 0x10000, 4, 32)
+    arr2 = (fp4q.SdSegment * 1)(seg2)
+    assert L.fp4q_sigma_delta_requant(arr2, 1, 4, 32, None) == 5                             # bank stride < 64
+    assert L.fp4q_balance_scale(fake16, 0, 4, 4, 4, fake16, 0, 4, 4, 1.5, fake16, fake16, None) == 5
+
+
+def test_device_check_without_gpu(fp4q):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host has a GPU")
+    fake16 = ctypes.c_void_p(0x10000)
+    st = fp4q.lib.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, fake16, fake16, 0, None)
+    assert st == 6
