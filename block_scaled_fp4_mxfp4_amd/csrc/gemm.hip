@@ -48,10 +48,10 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 128, BN = 128;
-constexpr int BK = 128;           // K elements per stage
+
+inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+constexpr int BK = 128;           // K elements per stage of the skinny kernel
 constexpr int BKB = BK / 2;       // code bytes per row per stage
-constexpr int LDR = BKB + 16;     // padded LDS row stride of a code tile (bytes)
 
 // ------------------------------------------------------------ dequant ----
 
@@ -106,257 +106,162 @@ __device__ __forceinline__ v8bf dequant8_bf16(uint32_t w, float sb) {
   return __builtin_bit_cast(v8bf, uint4{o[0], o[1], o[2], o[3]});
 }
 
-// ------------------------------------------------- stage load helpers ----
+// ====================================================== prefill GEMMs ====
+//
+// One kernel template for the three prefill formats.  A 256-thread workgroup
+// (2 x 2 wavefronts) owns a BM x BN output tile; each wavefront owns
+// (BM/2) x (BN/2), i.e. FM x FN fragments of 16 x 16.  K advances one LDS
+// stage at a time (register-staged double buffering, one barrier per
+// stage).  LDS code rows are padded by 16 bytes, which makes the 16-byte
+// fragment reads of eight consecutive rows land on disjoint banks.
+//
+// Tile order: the hardware hands workgroup b to XCD b % 8; each XCD is given
+// a contiguous range of tile ids, walked in groups of GROUP_M row tiles so
+// that the workgroups resident on one XCD share A rows and B columns in that
+// XCD's L2.
 
-// Copies rows [r0, r0 + 128) x 64 code bytes of stage kt into registers
-// (two 16-byte chunks per thread); rows past `rows` read as zero.
-struct CodeStage {
-  uint4 q[2];
+enum Fmt { FMT_MX = 0, FMT_NV = 1, FMT_W16 = 2 };
+
+struct GemmArgs {
+  const uint8_t* A;       // codes [M][K/2] (MX, NV) or bf16 [M][lda] (W16)
+  const uint8_t* As;      // A block scales (MX: [M][K/32], NV: [M][K/16]); unused for W16
+  const float* Ats;       // A tensor scale (NV)
+  const uint8_t* B;       // codes [N][K/2]
+  const uint8_t* Bs;      // B block scales
+  const float* Bts;       // B tensor scale (NV, W16)
+  int64_t M, N, K, lda;
+  float* Y;
+  int64_t ldy;
+  int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ void load_code_stage(CodeStage& st, const uint8_t* __restrict__ g,
-                                                int64_t r0, int64_t rows, int64_t ldb, int kt) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    const int64_t r = r0 + (c >> 2);
-    st.q[i] = r < rows ? *reinterpret_cast<const uint4*>(g + r * ldb + (int64_t)kt * BKB + (c & 3) * 16)
-                       : uint4{0u, 0u, 0u, 0u};
-  }
+constexpr int GROUP_M = 8;
+
+template <int FMT> struct FmtTraits;
+template <> struct FmtTraits<FMT_MX> {
+  static constexpr int BK = 256;                  // K elements per stage
+  static constexpr int SCB = BK / 32;             // scale bytes per row per stage
+};
+template <> struct FmtTraits<FMT_NV> {
+  static constexpr int BK = 128;
+  static constexpr int SCB = BK / 16;
+};
+template <> struct FmtTraits<FMT_W16> {
+  static constexpr int BK = 128;
+  static constexpr int SCB = BK / 16;
+};
+
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nt = tiles_m * tiles_n;
+  const int x = bid & 7, i = bid >> 3;
+  const int base = nt >> 3, rem = nt & 7;
+  const int t = x * base + (x < rem ? x : rem) + i;
+  const int per_group = GROUP_M * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+  const int in_g = t - group * per_group;
+  tm = first_m + in_g % gsz;
+  tn = in_g / gsz;
 }
 
-__device__ __forceinline__ void store_code_stage(const CodeStage& st, uint8_t* l) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    *reinterpret_cast<uint4*>(l + (c >> 2) * LDR + (c & 3) * 16) = st.q[i];
-  }
-}
+template <int FMT, int BM, int BN, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void k_gemm(const GemmArgs p) {
+  using T = FmtTraits<FMT>;
+  constexpr int BK = T::BK, SCB = T::SCB;
+  constexpr int CB = BK / 2;                                 // code bytes per row per stage
+  constexpr int LDC = CB + 16;                               // padded code row (bytes)
+  constexpr int ARB = (FMT == FMT_W16) ? BK * 2 : CB;        // A bytes per row per stage
+  constexpr int LDAR = ARB + 16;                             // padded A row (bytes)
+  constexpr int FM = BM / 32, FN = BN / 32;
+  constexpr int A_CH = BM * ARB / 16, B_CH = BN * CB / 16;   // 16-byte chunks per stage
+  constexpr int A_LD = (A_CH + kThreads - 1) / kThreads, B_LD = (B_CH + kThreads - 1) / kThreads;
+  constexpr int A_SC = (FMT == FMT_W16) ? 0 : BM;            // scale rows staged per stage
+  constexpr int SC_ROWS = A_SC + BN;
+  constexpr int SCW = SCB / 4;                               // scale words per row per stage
+  constexpr int SC_LD = (SC_ROWS * SCW + kThreads - 1) / kThreads;
 
-// ============================================================ MXFP4 ====
+  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDAR];
+  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDC];
+  __shared__ uint32_t lS[2][SC_ROWS * SCW];
 
-__global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, int64_t M, int64_t N, int64_t K, float* __restrict__ Y,
-    int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDR];
-  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDR];
-  __shared__ uint32_t lS[2][BM + BN];          // 4 E8M0 bytes per row per stage
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int64_t ldb = K / 2, lds = K / 32;
-  const int KT = (int)(K / BK);
+  int tm, tn;
+  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t ldb = p.K / 2, lds = p.K / (FMT == FMT_MX ? 32 : 16);
+  const int KT = (int)((p.K + BK - 1) / BK);   // the last stage may be half empty (K % BK == 128)
 
-  CodeStage sa, sb;
-  uint32_t ss = 0;
-  auto gload = [&](int kt) {
-    load_code_stage(sa, A, m0, M, ldb, kt);
-    load_code_stage(sb, B, n0, N, ldb, kt);
-    if (tid < BM) {
-      const int64_t r = m0 + tid;
-      ss = r < M ? *reinterpret_cast<const uint32_t*>(As + r * lds + kt * 4) : 0u;
-    } else {
-      const int64_t r = n0 + tid - BM;
-      ss = r < N ? *reinterpret_cast<const uint32_t*>(Bs + r * lds + kt * 4) : 0u;
-    }
-  };
-  auto sstore = [&](int buf) {
-    store_code_stage(sa, lA[buf]);
-    store_code_stage(sb, lB[buf]);
-    lS[buf][tid] = ss;
-  };
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    v8i af[4], bfr[4];
-    int sca[4], scb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 64 + i * 16 + r16;
-      const uint4 qa = *reinterpret_cast<const uint4*>(&lA[buf][ra * LDR + g * 16]);
-      af[i] = v8i{(int)qa.x, (int)qa.y, (int)qa.z, (int)qa.w, 0, 0, 0, 0};
-      sca[i] = (int)((lS[buf][ra] >> (8 * g)) & 0xFFu);
-      const int rb = wn * 64 + i * 16 + r16;
-      const uint4 qb = *reinterpret_cast<const uint4*>(&lB[buf][rb * LDR + g * 16]);
-      bfr[i] = v8i{(int)qb.x, (int)qb.y, (int)qb.z, (int)qb.w, 0, 0, 0, 0};
-      scb[i] = (int)((lS[buf][BM + rb] >> (8 * g)) & 0xFFu);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bfr[j], acc[i][j], 4, 4, 0,
-                                                                     sca[i], 0, scb[j]);
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 16 + g * 4 + r;
-        const int64_t col = n0 + wn * 64 + j * 16 + r16;
-        if (row < M && col < N) Y[row * ldy + col] = acc[i][j][r];
-      }
-}
-
-// ============================================================ NVFP4 ====
-
-__global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
-    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
-    int64_t M, int64_t N, int64_t K, float* __restrict__ Y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDR];
-  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDR];
-  __shared__ uint2 lS[2][BM + BN];             // 8 E4M3 bytes per row per stage
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int64_t ldb = K / 2, lds = K / 16;
-  const int KT = (int)(K / BK);
-
-  CodeStage sa, sb;
-  uint2 ss = {0u, 0u};
-  auto gload = [&](int kt) {
-    load_code_stage(sa, A, m0, M, ldb, kt);
-    load_code_stage(sb, B, n0, N, ldb, kt);
-    if (tid < BM) {
-      const int64_t r = m0 + tid;
-      ss = r < M ? *reinterpret_cast<const uint2*>(As + r * lds + kt * 8) : uint2{0u, 0u};
-    } else {
-      const int64_t r = n0 + tid - BM;
-      ss = r < N ? *reinterpret_cast<const uint2*>(Bs + r * lds + kt * 8) : uint2{0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-    store_code_stage(sa, lA[buf]);
-    store_code_stage(sb, lB[buf]);
-    lS[buf][tid] = ss;
-  };
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    uint4 qa[4], qb[4];
-    ScaleSplit xa[4][2], xb[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 64 + i * 16 + r16;
-      qa[i] = *reinterpret_cast<const uint4*>(&lA[buf][ra * LDR + g * 16]);
-      const uint2 sa2 = lS[buf][ra];
-      const uint32_t wa = (g < 2 ? sa2.x : sa2.y) >> (16 * (g & 1));
-      xa[i][0] = split_e4m3(wa & 0xFFu);
-      xa[i][1] = split_e4m3((wa >> 8) & 0xFFu);
-      const int rb = wn * 64 + i * 16 + r16;
-      qb[i] = *reinterpret_cast<const uint4*>(&lB[buf][rb * LDR + g * 16]);
-      const uint2 sb2 = lS[buf][BM + rb];
-      const uint32_t wb = (g < 2 ? sb2.x : sb2.y) >> (16 * (g & 1));
-      xb[i][0] = split_e4m3(wb & 0xFFu);
-      xb[i][1] = split_e4m3((wb >> 8) & 0xFFu);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v8h ha[4], hb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wa = s == 0 ? qa[i].x : s == 1 ? qa[i].y : s == 2 ? qa[i].z : qa[i].w;
-        const uint32_t wb = s == 0 ? qb[i].x : s == 1 ? qb[i].y : s == 2 ? qb[i].z : qb[i].w;
-        ha[i] = dequant8_f16(wa, xa[i][s >> 1]);
-        hb[i] = dequant8_f16(wb, xb[i][s >> 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i], hb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
-  }
-  const float tsc = (*Ats) * (*Bts);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 16 + g * 4 + r;
-        const int64_t col = n0 + wn * 64 + j * 16 + r16;
-        if (row < M && col < N) Y[row * ldy + col] = acc[i][j][r] * tsc;
-      }
-}
-
-// ============================================================ W4A16 ====
-
-constexpr int LDA16 = BK * 2 + 16;   // padded LDS row stride of a bf16 A stage (bytes)
-
-__global__ __launch_bounds__(kThreads) void k_gemm_w4a16(
-    const uint16_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const float* __restrict__ Bts, int64_t M, int64_t N, int64_t K,
-    float* __restrict__ Y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t lA[2][BM * LDA16];
-  __shared__ __attribute__((aligned(16))) uint8_t lB[2][BN * LDR];
-  __shared__ uint2 lS[2][BN];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int64_t ldb = K / 2, lds = K / 16;
-  const int KT = (int)(K / BK);
-
-  uint4 ra[8];
-  CodeStage sb;
-  uint2 ss = {0u, 0u};
+  uint4 ra[A_LD], rb[B_LD];
+  uint32_t rs[SC_LD];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {         // 128 rows x 256 bytes = 2048 chunks
+    for (int i = 0; i < A_LD; ++i) {
       const int c = tid + kThreads * i;
-      const int64_t r = m0 + (c >> 4);
-      ra[i] = r < M ? *reinterpret_cast<const uint4*>(A + r * lda + (int64_t)kt * BK + (c & 15) * 8)
-                    : uint4{0u, 0u, 0u, 0u};
+      constexpr int CPR = ARB / 16;
+      const int64_t r = m0 + c / CPR;
+      uint4 v = {0u, 0u, 0u, 0u};
+      const int64_t kb = (int64_t)kt * ARB + (c % CPR) * 16;    // byte offset within the row
+      if (c < A_CH && r < p.M && kb < (FMT == FMT_W16 ? p.K * 2 : ldb)) {
+        if constexpr (FMT == FMT_W16)
+          v = *reinterpret_cast<const uint4*>(p.A + (r * p.lda + (int64_t)kt * BK) * 2 + (c % CPR) * 16);
+        else
+          v = *reinterpret_cast<const uint4*>(p.A + r * ldb + (int64_t)kt * CB + (c % CPR) * 16);
+      }
+      ra[i] = v;
     }
-    load_code_stage(sb, B, n0, N, ldb, kt);
-    if (tid < BN) {
-      const int64_t r = n0 + tid;
-      ss = r < N ? *reinterpret_cast<const uint2*>(Bs + r * lds + kt * 8) : uint2{0u, 0u};
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int c = tid + kThreads * i;
+      constexpr int CPR = CB / 16;
+      const int64_t r = n0 + c / CPR;
+      uint4 v = {0u, 0u, 0u, 0u};
+      const int64_t kb = (int64_t)kt * CB + (c % CPR) * 16;
+      if (c < B_CH && r < p.N && kb < ldb) v = *reinterpret_cast<const uint4*>(p.B + r * ldb + kb);
+      rb[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < SC_LD; ++i) {
+      const int c = tid + kThreads * i;            // (row, word) of the staged scales
+      const int row = c / SCW, w = c % SCW;
+      const int64_t kb = (int64_t)kt * SCB + 4 * w;
+      uint32_t v = 0u;
+      if (row < A_SC) {
+        const int64_t r = m0 + row;
+        if (r < p.M && kb < lds) v = *reinterpret_cast<const uint32_t*>(p.As + r * lds + kb);
+      } else if (row < SC_ROWS) {
+        const int64_t r = n0 + (row - A_SC);
+        if (r < p.N && kb < lds) v = *reinterpret_cast<const uint32_t*>(p.Bs + r * lds + kb);
+      }
+      rs[i] = v;
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < A_LD; ++i) {
       const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(&lA[buf][(c >> 4) * LDA16 + (c & 15) * 16]) = ra[i];
+      constexpr int CPR = ARB / 16;
+      if (c < A_CH) *reinterpret_cast<uint4*>(&lA[buf][(c / CPR) * LDAR + (c % CPR) * 16]) = ra[i];
     }
-    store_code_stage(sb, lB[buf]);
-    if (tid < BN) lS[buf][tid] = ss;
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int c = tid + kThreads * i;
+      constexpr int CPR = CB / 16;
+      if (c < B_CH) *reinterpret_cast<uint4*>(&lB[buf][(c / CPR) * LDC + (c % CPR) * 16]) = rb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SC_LD; ++i) {
+      const int c = tid + kThreads * i;
+      if (c < SC_ROWS * SCW) lS[buf][c] = rs[i];
+    }
   };
 
-  v4f acc[4][4];
+  v4f acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   gload(0);
   sstore(0);
@@ -364,49 +269,110 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a16(
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < KT) gload(kt + 1);
-    uint4 qb[4];
-    float sbv[4][2];
+    const uint8_t* la = lA[buf];
+    const uint8_t* lb = lB[buf];
+    if constexpr (FMT == FMT_MX) {
+      // two 128-element instruction steps per stage; lane group g owns
+      // bytes [16 g, 16 g + 16) of each 64-byte half
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rb = wn * 64 + j * 16 + r16;
-      qb[j] = *reinterpret_cast<const uint4*>(&lB[buf][rb * LDR + g * 16]);
-      const uint2 s2 = lS[buf][rb];
-      const uint32_t w = (g < 2 ? s2.x : s2.y) >> (16 * (g & 1));
-      sbv[j][0] = e4m3_decode(w & 0xFFu);
-      sbv[j][1] = e4m3_decode((w >> 8) & 0xFFu);
-    }
+      for (int ks = 0; ks < 2; ++ks) {
+        v8i af[FM];
+        int sa[FM];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v8bf ha[4], hb[4];
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm * (BM / 2) + i * 16 + r16;
+          const uint4 q = *reinterpret_cast<const uint4*>(la + row * LDAR + ks * 64 + g * 16);
+          af[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          sa[i] = (int)((reinterpret_cast<const uint8_t*>(&lS[buf][row * SCW]))[ks * 4 + g]);
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_ = wm * 64 + i * 16 + r16;
-        ha[i] = *reinterpret_cast<const v8bf*>(&lA[buf][ra_ * LDA16 + (32 * g + 8 * s) * 2]);
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * (BN / 2) + j * 16 + r16;
+          const uint4 q = *reinterpret_cast<const uint4*>(lb + row * LDC + ks * 64 + g * 16);
+          const v8i bf = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          const int sb = (int)((reinterpret_cast<const uint8_t*>(&lS[buf][(A_SC + row) * SCW]))[ks * 4 + g]);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf, acc[i][j], 4, 4, 0, sa[i], 0, sb);
+        }
       }
+    } else {
+      // lane group g owns elements [32 g, 32 g + 32) of the stage: two
+      // NVFP4 blocks (h = 0, 1), each consumed as two 8-element slices
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = s == 0 ? qb[j].x : s == 1 ? qb[j].y : s == 2 ? qb[j].z : qb[j].w;
-        hb[j] = dequant8_bf16(w, sbv[j][s >> 1]);
+      for (int h = 0; h < 2; ++h) {
+        uint2 qa[FM];
+        ScaleSplit xa[FM];
+        if constexpr (FMT == FMT_NV) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * (BM / 2) + i * 16 + r16;
+            qa[i] = *reinterpret_cast<const uint2*>(la + row * LDAR + g * 16 + h * 8);
+            xa[i] = split_e4m3((reinterpret_cast<const uint8_t*>(&lS[buf][row * SCW]))[2 * g + h]);
+          }
+        }
+        uint2 qb[FN];
+        ScaleSplit xb[FN];
+        float sbf[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * (BN / 2) + j * 16 + r16;
+          qb[j] = *reinterpret_cast<const uint2*>(lb + row * LDC + g * 16 + h * 8);
+          const uint32_t sbyte = (reinterpret_cast<const uint8_t*>(&lS[buf][(A_SC + row) * SCW]))[2 * g + h];
+          if constexpr (FMT == FMT_NV) xb[j] = split_e4m3(sbyte);
+          else sbf[j] = e4m3_decode(sbyte);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if constexpr (FMT == FMT_NV) {
+            v8h ha[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ha[i] = dequant8_f16(s2 ? qa[i].y : qa[i].x, xa[i]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const v8h hb = dequant8_f16(s2 ? qb[j].y : qb[j].x, xb[j]);
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i], hb, acc[i][j], 0, 0, 0);
+            }
+          } else {
+            const int s = 2 * h + s2;
+            v8bf ha[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              const int row = wm * (BM / 2) + i * 16 + r16;
+              ha[i] = *reinterpret_cast<const v8bf*>(la + row * LDAR + (32 * g + 8 * s) * 2);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const v8bf hb = dequant8_bf16(s2 ? qb[j].y : qb[j].x, sbf[j]);
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[i], hb, acc[i][j], 0, 0, 0);
+            }
+          }
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[i], hb[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  const float tsc = *Bts;
+  float tsc = 1.0f;
+  if constexpr (FMT == FMT_NV) tsc = (*p.Ats) * (*p.Bts);
+  if constexpr (FMT == FMT_W16) tsc = *p.Bts;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 16 + g * 4 + r;
-        const int64_t col = n0 + wn * 64 + j * 16 + r16;
-        if (row < M && col < N) Y[row * ldy + col] = acc[i][j][r] * tsc;
+        const int64_t row = m0 + wm * (BM / 2) + i * 16 + g * 4 + r;
+        const int64_t col = n0 + wn * (BN / 2) + j * 16 + r16;
+        if (row < p.M && col < p.N) {
+          float v = acc[i][j][r];
+          if constexpr (FMT != FMT_MX) v = v * tsc;
+          p.Y[row * p.ldy + col] = v;
+        }
       }
 }
 
@@ -550,32 +516,49 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4_skinny(
   }
 }
 
-inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
-
 }  // namespace
 
-hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
-                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
-                             int64_t ldy, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_mxfp4, dim3(cdiv(N, BN), cdiv(M, BM)), dim3(kThreads), 0, s, a, as, b, bs, M,
-                     N, K, y, ldy);
+// Tile shapes (BM, BN, minimum workgroups per CU) of the prefill kernels.
+#ifndef FP4Q_MX_TILE
+#define FP4Q_MX_TILE 128, 224, 1
+#endif
+#ifndef FP4Q_NV_TILE
+#define FP4Q_NV_TILE 128, 256, 1
+#endif
+#ifndef FP4Q_W16_TILE
+#define FP4Q_W16_TILE 256, 128, 1
+#endif
+
+namespace {
+template <int FMT, int BM, int BN, int MINB>
+hipError_t launch_tiled(const GemmArgs& a0, hipStream_t s) {
+  GemmArgs a = a0;
+  a.tiles_m = (int)cdiv(a.M, BM);
+  a.tiles_n = (int)cdiv(a.N, BN);
+  hipLaunchKernelGGL((k_gemm<FMT, BM, BN, MINB>), dim3((unsigned)a.tiles_m * a.tiles_n), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
+}  // namespace
 
-hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
+hipError_t launch_gemm_mxfp4_staged(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                    const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
+                                    int64_t ldy, hipStream_t s) {
+  GemmArgs p{a, as, nullptr, b, bs, nullptr, M, N, K, 0, y, ldy, 0, 0};
+  return launch_tiled<FMT_MX, FP4Q_MX_TILE>(p, s);
+}
+
+hipError_t launch_gemm_nvfp4_staged(const uint8_t* a, const uint8_t* as, const float* ats,
                              const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
                              int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_nvfp4, dim3(cdiv(N, BN), cdiv(M, BM)), dim3(kThreads), 0, s, a, as, ats, b,
-                     bs, bts, M, N, K, y, ldy);
-  return hipGetLastError();
+  GemmArgs p{a, as, ats, b, bs, bts, M, N, K, 0, y, ldy, 0, 0};
+  return launch_tiled<FMT_NV, FP4Q_NV_TILE>(p, s);
 }
 
 hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
                              const float* bts, int64_t M, int64_t N, int64_t K, float* y,
                              int64_t ldy, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemm_w4a16, dim3(cdiv(N, BN), cdiv(M, BM)), dim3(kThreads), 0, s,
-                     reinterpret_cast<const uint16_t*>(a), lda, b, bs, bts, M, N, K, y, ldy);
-  return hipGetLastError();
+  GemmArgs p{reinterpret_cast<const uint8_t*>(a), nullptr, nullptr, b, bs, bts, M, N, K, lda, y, ldy, 0, 0};
+  return launch_tiled<FMT_W16, FP4Q_W16_TILE>(p, s);
 }
 
 bool skinny_supported(int64_t K) { return K <= SK_MAXK; }

@@ -1,0 +1,407 @@
+// gemm_mx.hip -- MXFP4 W4A4 prefill GEMM on gfx950's block-scaled FP4
+// matrix cores ("MACaQ", core method: y = [(x*t)B]_MXFP4 W'^T_MXFP4).
+//
+// Each v_mfma_scale_f32_16x16x128_f8f6f4 consumes, per lane, 32 packed E2M1
+// codes of one row and the E8M0 byte of exactly that 32-element block, so
+// the OCP MXFP4 tensors feed the instruction as stored: no dequantization.
+//
+// Data movement (the part that decides speed here):
+//  * a 256-thread workgroup owns a BM x BN tile (256 x 224 or 256 x 256);
+//    its four wavefronts own 128 x BN/2 each, i.e. 8 x (BN/32) 16 x 16
+//    accumulator tiles, so every 16-byte fragment read from LDS feeds BN/32
+//    or 8 matrix instructions;
+//  * K advances 256 elements (one whole 128-byte line of codes per row) per
+//    stage through a two-slot LDS ring filled by direct global->LDS loads
+//    (global_load_lds, 16 bytes per lane) issued one stage ahead, so no
+//    registers are spent on staging and the loads of stage k + 1 overlap
+//    the 2 x 8 x (BN/32) matrix instructions of stage k;
+//  * a row's eight 16-byte chunks are stored XOR-swizzled by
+//    (row ^ ((row >> 3) & 1)) & 7, which puts the 16-byte fragment reads of
+//    16 consecutive rows on disjoint banks whether the LDS serves 128 or
+//    256 bytes per clock;
+//  * rows past M or N are loaded from the last valid row (their results are
+//    never stored), so every lane issues the same number of loads and the
+//    wait counts are compile-time constants;
+//  * the fp32 output leaves through LDS: each wavefront re-stages 16-row
+//    strips of its accumulators and writes whole rows with 16-byte
+//    non-temporal stores (scattered 4-byte lane stores ran at ~2.3 TB/s and
+//    cost as much time as the whole K loop).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace fp4q {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+enum { FMT_MX = 0, FMT_NV = 1 };
+
+// E4M3 block scale (non-negative byte) -> the same value in fp16, splatted
+// to both halves.  Every E4M3 value is an fp16 normal: (b << 7) + 0x2000
+// re-biases a normal E4M3 exponent (7 -> 15); subnormal E4M3 bytes (< 8)
+// are b * 2^-9.
+__device__ __forceinline__ v2h e4m3_to_h2(uint32_t b) {
+  const uint32_t sub = __builtin_bit_cast(uint16_t, (_Float16)((float)b * 0.001953125f));
+  const uint32_t h = b >= 8u ? (b << 7) + 0x2000u : sub;
+  return __builtin_bit_cast(v2h, h | (h << 16));
+}
+
+// 8 NVFP4 codes (one dword) -> 8 exact fp16 values code * s_b: the convert
+// gives the code value exactly, the product has at most 2 + 4 significant
+// bits and lies in [2^-10, 2688].
+__device__ __forceinline__ v8h dequant8(uint32_t w, v2h sb) {
+  const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * sb);
+  const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * sb);
+  const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * sb);
+  const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * sb);
+  return __builtin_bit_cast(v8h, uint4{o0, o1, o2, o3});
+}
+
+constexpr int kThreads = 256;
+constexpr int NS = 2;         // LDS ring slots
+
+struct MxArgs {
+  const uint8_t* A;
+  const uint8_t* As;
+  const uint8_t* B;
+  const uint8_t* Bs;
+  const float* Ats;             // NVFP4 tensor scales (unused for MXFP4)
+  const float* Bts;
+  int64_t M, N, K;
+  float* Y;
+  int64_t ldy;
+  int tiles_m, tiles_n;
+};
+
+constexpr int GROUP_M = 8;
+
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nt = tiles_m * tiles_n;
+  const int x = bid & 7, i = bid >> 3;
+  const int base = nt >> 3, rem = nt & 7;
+  const int t = x * base + (x < rem ? x : rem) + i;     // contiguous tile range per XCD
+  const int per_group = GROUP_M * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+  const int in_g = t - group * per_group;
+  tm = first_m + in_g % gsz;
+  tn = in_g / gsz;
+}
+
+// XOR swizzle of the 16-byte chunks of a staged row (CB / 16 chunks).  It
+// depends on row % 16 only, so one value per lane serves every fragment,
+// and it keeps the 16-byte reads of 16 consecutive rows on disjoint banks
+// for 128- and 256-byte-per-clock LDS alike.
+template <int CB>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CB == 128) return (row ^ ((row >> 3) & 1)) & 7;
+  else return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+// Direct global->LDS loads (gfx950 global_load_lds): lane l of the wave
+// writes its 16 (or 4) bytes at LDS byte address m0 + 16 l (or 4 l).  They
+// are issued from inline assembly so that the compiler does not serialise
+// them against the LDS reads of other ring slots; ordering is explicit
+// (s_waitcnt vmcnt + s_barrier below).  The instructions have no register
+// results; the address registers are consumed at issue.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p);
+}
+// Address = uniform 64-bit base (SGPRs) + per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(off), "s"(base) : "memory");
+}
+
+template <int FMT, int BM, int BN, int CB>
+struct MxLayout {
+  static constexpr int B_ROWS = ((BN + 63) / 64) * 64;   // whole 64-row load instructions
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = A_OFF + BM * CB;
+  static constexpr int SA_OFF = B_OFF + B_ROWS * CB;
+  static constexpr int SCB = FMT == FMT_MX ? CB / 16 : CB / 8;  // scale bytes per row per stage
+  static constexpr int SB_OFF = SA_OFF + BM * SCB;
+  static constexpr int STAGE = SB_OFF + B_ROWS * SCB;
+  static constexpr int A_LD = BM * CB / 16 / kThreads;        // 16-byte loads per thread
+  static constexpr int B_LD = B_ROWS * CB / 16 / kThreads;
+  static constexpr int SA_LD = (BM * SCB / 4 + kThreads - 1) / kThreads;      // 4-byte loads per thread
+  static constexpr int SB_LD = (B_ROWS * SCB / 4 + kThreads - 1) / kThreads;
+  static constexpr int SA_N = BM * SCB / 4, SB_N = B_ROWS * SCB / 4;         // 4-byte words to load
+  static constexpr int LOADS = A_LD + B_LD + SA_LD + SB_LD;   // per thread per stage
+};
+
+template <int FMT, int BM, int BN, int CB, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
+  using Lay = MxLayout<FMT, BM, BN, CB>;
+  constexpr int CPR = CB / 16;                    // 16-byte chunks per staged row
+  constexpr int KS = CB / 64;                     // 128-element instruction steps per stage
+  static_assert((BM == 128 || BM == 256) && (BN == 160 || BN == 224 || BN == 256) && (CB == 64 || CB == 128), "tile");
+  static_assert(Lay::SA_N % 64 == 0 && Lay::SB_N % 64 == 0, "whole-wave scale loads");
+  constexpr int FM = BM / 32, FN = BN / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * Lay::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
+  int tm, tn;
+  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t ldb = p.K / 2, lds = p.K / (FMT == FMT_MX ? 32 : 16);
+  const int KT = (int)(p.K / (2 * CB));
+
+  // ---- per-thread byte offsets of the direct loads (row and chunk are
+  // fixed over K; the stage adds kt * 128 bytes of codes / 8 of scales).
+  uint32_t offA[Lay::A_LD], offB[Lay::B_LD], offSA[Lay::SA_LD], offSB[Lay::SB_LD];
+#pragma unroll
+  for (int i = 0; i < Lay::A_LD; ++i) {
+    const int s = i * kThreads + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
+    int64_t r = m0 + row;
+    r = r < p.M ? r : p.M - 1;
+    offA[i] = (uint32_t)(r * ldb + gch * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < Lay::B_LD; ++i) {
+    const int s = i * kThreads + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
+    int64_t r = n0 + row;
+    r = r < p.N ? r : p.N - 1;
+    offB[i] = (uint32_t)(r * ldb + gch * 16);
+  }
+  // scales: SCB bytes per row per stage, one 4-byte word per lane
+  constexpr int WPR = Lay::SCB / 4;               // words per row per stage
+#pragma unroll
+  for (int i = 0; i < Lay::SA_LD; ++i) {
+    const int s = i * kThreads + tid;
+    int64_t r = m0 + s / WPR;
+    r = r < p.M ? r : p.M - 1;
+    offSA[i] = (uint32_t)(r * lds + (s % WPR) * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < Lay::SB_LD; ++i) {
+    const int s = i * kThreads + tid;
+    int64_t r = n0 + s / WPR;
+    r = r < p.N ? r : p.N - 1;
+    offSB[i] = (uint32_t)(r * lds + (s % WPR) * 4);
+  }
+
+  const uint32_t smem_base = lds_offset(smem);
+  auto issue = [&](int kt) {
+    const uint32_t st = smem_base + (uint32_t)((kt % NS) * Lay::STAGE);
+    const uint32_t kc = (uint32_t)kt * CB, ksc = (uint32_t)kt * Lay::SCB;
+#pragma unroll
+    for (int i = 0; i < Lay::A_LD; ++i) dma16(p.A, offA[i] + kc, st + Lay::A_OFF + (i * kThreads + wave * 64) * 16);
+#pragma unroll
+    for (int i = 0; i < Lay::B_LD; ++i) dma16(p.B, offB[i] + kc, st + Lay::B_OFF + (i * kThreads + wave * 64) * 16);
+#pragma unroll
+    for (int i = 0; i < Lay::SA_LD; ++i)
+      if (i * kThreads + wave * 64 < Lay::SA_N)          // wave-uniform
+        dma4(p.As, offSA[i] + ksc, st + Lay::SA_OFF + (i * kThreads + wave * 64) * 4);
+#pragma unroll
+    for (int i = 0; i < Lay::SB_LD; ++i)
+      if (i * kThreads + wave * 64 < Lay::SB_N)
+        dma4(p.Bs, offSB[i] + ksc, st + Lay::SB_OFF + (i * kThreads + wave * 64) * 4);
+  };
+
+  struct Frags {
+    v8i a[FM], b[FN];
+    int sa[FM], sb[FN];
+  };
+  // fragments of instruction step ks (K elements [128 ks, 128 ks + 128) of
+  // the stage): lane group g reads 16-byte chunk 4 ks + g of its row
+  auto load_frags = [&](Frags& f, int kt, int ks) {
+    const uint8_t* st = smem + (kt % NS) * Lay::STAGE;
+    const int c = ks * 4 + g;                      // chunk within the staged row
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * (BM / 2) + i * 16 + r16;
+      const uint4 q = *reinterpret_cast<const uint4*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+      f.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      f.sa[i] = st[Lay::SA_OFF + row * Lay::SCB + c];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * (BN / 2) + j * 16 + r16;
+      const uint4 q = *reinterpret_cast<const uint4*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+      f.b[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      f.sb[j] = st[Lay::SB_OFF + row * Lay::SCB + c];
+    }
+  };
+
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 0, f.sa[i],
+                                                                     0, f.sb[j]);
+  };
+
+  // Stage kt lives in ring slot kt % 2.  At the top of iteration kt only
+  // the loads of stage kt are in flight; after the wait and the barrier
+  // they are visible to every wave and every wave has finished reading
+  // slot (kt + 1) % 2 (stage kt - 1), which then receives stage kt + 1.
+  // (A plain s_barrier, not __syncthreads: its release fence would also
+  // wait for loads that are meant to stay in flight.)
+  issue(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < KT) issue(kt + 1);
+    if constexpr (FMT == FMT_MX) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks) __builtin_amdgcn_sched_barrier(0);   // keep one step of fragments live
+        Frags f;
+        load_frags(f, kt, ks);
+        mma(f);
+      }
+    } else {
+      // NVFP4: lane group g owns elements [32 c, 32 c + 32) of chunk c; each
+      // half h is one 16-element block, consumed as two 8-element slices by
+      // the fp16 instruction (the same element assignment for A and B).
+      const uint8_t* st = smem + (kt % NS) * Lay::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks * 4 + g;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (ks | h) __builtin_amdgcn_sched_barrier(0);
+          uint2 qa[FM], qb[FN];
+          v2h sa[FM], sb[FN];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * (BM / 2) + i * 16 + r16;
+            qa[i] = *reinterpret_cast<const uint2*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4) + 8 * h);
+            sa[i] = e4m3_to_h2(st[Lay::SA_OFF + row * Lay::SCB + 2 * c + h]);
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int row = wn * (BN / 2) + j * 16 + r16;
+            qb[j] = *reinterpret_cast<const uint2*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4) + 8 * h);
+            sb[j] = e4m3_to_h2(st[Lay::SB_OFF + row * Lay::SCB + 2 * c + h]);
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            v8h ha[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ha[i] = dequant8(s2 ? qa[i].y : qa[i].x, sa[i]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const v8h hb = dequant8(s2 ? qb[j].y : qb[j].x, sb[j]);
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i], hb, acc[i][j], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: each wavefront stages one 16-row strip of its tile at a
+  // time in its own LDS area and writes whole rows with 16-byte stores
+  // (the fp32 output is the largest stream of the kernel).
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();                   // ring slots no longer read
+  constexpr int WC = BN / 2;                      // columns per wavefront
+  constexpr int LDE = WC + 4;                     // padded staging row (floats)
+  float* stage = reinterpret_cast<float*>(smem) + wave * 16 * LDE;
+  const int64_t col0 = n0 + wn * WC;
+  const bool vec = ((p.ldy & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.Y) & 15) == 0);
+  const float tsc = FMT == FMT_NV ? (*p.Ats) * (*p.Bts) : 1.0f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[i][j][r];
+        if constexpr (FMT == FMT_NV) v = v * tsc;
+        stage[(g * 4 + r) * LDE + j * 16 + r16] = v;
+      }
+    const int64_t row0 = m0 + wm * (BM / 2) + i * 16;
+#pragma unroll
+    for (int k = 0; k < (16 * WC / 4 + 63) / 64; ++k) {
+      const int idx = k * 64 + lane;
+      if (idx < 16 * WC / 4) {
+        const int rr = idx / (WC / 4), c4 = (idx % (WC / 4)) * 4;
+        const v4f v = *reinterpret_cast<const v4f*>(&stage[rr * LDE + c4]);
+        const int64_t row = row0 + rr, col = col0 + c4;
+        if (row < p.M) {
+          float* dst = p.Y + row * p.ldy + col;
+          if (vec && col + 4 <= p.N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(dst));
+          } else {
+            if (col + 0 < p.N) dst[0] = v[0];
+            if (col + 1 < p.N) dst[1] = v[1];
+            if (col + 2 < p.N) dst[2] = v[2];
+            if (col + 3 < p.N) dst[3] = v[3];
+          }
+        }
+      }
+    }
+  }
+}
+
+#ifndef FP4Q_MX_BM
+#define FP4Q_MX_BM 256        // workgroup rows
+#define FP4Q_MX_CB 128        // code bytes per row per stage
+#define FP4Q_MX_MINB 1        // workgroups per CU the register budget targets
+#endif
+#ifndef FP4Q_NV_BM
+#define FP4Q_NV_BM 256
+#define FP4Q_NV_BN 160
+#define FP4Q_NV_CB 64
+#endif
+
+inline int cdiv_i(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+template <int FMT, int BM, int BN, int CB, int MINB>
+hipError_t launch_mx3(const MxArgs& a0, hipStream_t s) {
+  MxArgs a = a0;
+  a.tiles_m = cdiv_i(a.M, BM);
+  a.tiles_n = cdiv_i(a.N, BN);
+  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
+                             int64_t ldy, hipStream_t s) {
+  MxArgs p{a, as, b, bs, nullptr, nullptr, M, N, K, y, ldy, 0, 0};
+  // K % 256 == 128 or tensors past 4 GiB: the register-staged kernel.
+  if (K % (2 * FP4Q_MX_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
+    return launch_gemm_mxfp4_staged(a, as, b, bs, M, N, K, y, ldy, s);
+  // 224 divides the common 7 * 2^k widths exactly; otherwise 256.
+  if (N % 224 == 0 && N % 256 != 0) return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB>(p, s);
+  return launch_mx3<FMT_MX, FP4Q_MX_BM, 256, FP4Q_MX_CB, FP4Q_MX_MINB>(p, s);
+}
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
+                             const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
+                             int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s) {
+  if (K % (2 * FP4Q_NV_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
+    return launch_gemm_nvfp4_staged(a, as, ats, b, bs, bts, M, N, K, y, ldy, s);
+  MxArgs p{a, as, b, bs, ats, bts, M, N, K, y, ldy, 0, 0};
+  return launch_mx3<FMT_NV, FP4Q_NV_BM, FP4Q_NV_BN, FP4Q_NV_CB, 1>(p, s);
+}
+
+}  // namespace fp4q

@@ -30,6 +30,13 @@ hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
 hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
                              int64_t ldy, hipStream_t s);
+// Register-staged MXFP4 kernel for shapes the direct-load kernel does not take.
+hipError_t launch_gemm_mxfp4_staged(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                    const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,
+                                    int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_nvfp4_staged(const uint8_t* a, const uint8_t* as, const float* ats,
+                                    const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
+                                    int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
                              const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
                              int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s);
