@@ -13,8 +13,11 @@ namespace fp4q {
 hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
                               hipStream_t s);
+// Writes max|x| into the tensor-scale cell (amax encoding).  scratch (may be
+// NULL with scratch_bytes == 0) holds per-workgroup partial maxima when it
+// is large enough; its contents are destroyed.
 hipError_t launch_amax_to_cell(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
-                               float* cell, hipStream_t s);
+                               float* cell, uint8_t* scratch, int64_t scratch_bytes, hipStream_t s);
 hipError_t launch_quant_mxfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                               const float* chan_scale, int hadamard, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);

@@ -54,10 +54,17 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float v[8])
   }
 }
 
-__device__ __forceinline__ uint32_t pack8(const uint32_t c[8]) {
+// Eight values -> eight packed E2M1 codes (element 2i in the low nibble of
+// byte i) with v_cvt_scalef32_pk_fp4_f32 at scale 1.0: round to nearest,
+// ties to the even code, saturation at +-6, sign of zero kept -- the same
+// function as e2m1_encode() (checked exhaustively near every decision point
+// and on random finite inputs), two elements per instruction.
+__device__ __forceinline__ uint32_t encode8_scaled(const float v[8], float rho) {
   uint32_t p = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p |= (c[i] & 0xFu) << (4 * i);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0] * rho, v[1] * rho, 1.0f, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2] * rho, v[3] * rho, 1.0f, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4] * rho, v[5] * rho, 1.0f, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6] * rho, v[7] * rho, 1.0f, 3);
   return p;
 }
 
@@ -83,19 +90,36 @@ __device__ __forceinline__ int64_t chunk_offset(int64_t c, int64_t cpr, int64_t 
 
 // ---------------------------------------------------------------- amax ----
 
-__global__ void k_cell_reset(uint32_t* cell) { *cell = kAmaxFlag; }
+// Tensor maximum in two steps without atomics (many workgroups updating
+// one address serialise in L2): each workgroup writes the bit pattern of
+// its partial max|x| to partial[blockIdx.x]; a one-workgroup finalize
+// kernel reduces the partials into the tensor-scale cell (amax encoding).
+// With direct != 0 (single workgroup) the cell is written at once.
+constexpr int kAmaxUnroll = 8;
+constexpr int kAmaxMaxGrid = 2048;
 
 template <bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t nchunks,
                                                    int64_t cpr, int64_t ld,
-                                                   uint32_t* __restrict__ cell) {
+                                                   uint32_t* __restrict__ out, int direct) {
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    float v[8];
-    load8<BF16>(x, chunk_offset<CONTIG>(c, cpr, ld), v);
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kAmaxUnroll;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * kAmaxUnroll + threadIdx.x; c0 < nchunks; c0 += stride) {
+    float v[kAmaxUnroll][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+    for (int u = 0; u < kAmaxUnroll; ++u) {           // all loads first
+      const int64_t c = c0 + (int64_t)u * kThreads;
+      if (c < nchunks) {
+        load8<BF16>(x, chunk_offset<CONTIG>(c, cpr, ld), v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[u][i]));
   }
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   __shared__ float red[kThreads / 64];
@@ -104,7 +128,23 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, red[i]);
-    atomicMax(cell, kAmaxFlag | __float_as_uint(m));
+    if (direct) out[0] = kAmaxFlag | __float_as_uint(m);
+    else out[blockIdx.x] = __float_as_uint(m);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __restrict__ partial, int n,
+                                                            uint32_t* __restrict__ cell) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partial[i]);   // non-negative floats
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+    *cell = kAmaxFlag | m;
   }
 }
 
@@ -140,11 +180,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     if (a > 0.0f && st > 0.0f) sb = e4m3_ceil(a / six_st);
     const float s = st * e4m3_decode(sb);
     const float rho = 1.0f / s;
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = (s == 0.0f) ? 0u : e2m1_encode(v[u][i] * rho);
+    const uint32_t p = (s == 0.0f) ? 0u : encode8_scaled(v[u], rho);
     if (cidx[u] < nchunks) {
-      codes[cidx[u]] = pack8(c);
+      codes[cidx[u]] = p;
       if (!(cidx[u] & 1)) scales[cidx[u] >> 1] = (uint8_t)sb;
     }
   }
@@ -228,11 +266,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     const bool zero = !(a > 0.0f);
     const int32_t e = zero ? -127 : mx_block_exponent(a);
     const float inv = pow2_neg(e);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = zero ? 0u : e2m1_encode(v[u][i] * inv);
+    const uint32_t p = zero ? 0u : encode8_scaled(v[u], inv);
     if (cidx[u] < nchunks) {
-      codes[cidx[u]] = pack8(c);
+      codes[cidx[u]] = p;
       if (qlane == 0) scales[cidx[u] >> 2] = (uint8_t)(e + 127);
     }
   }
@@ -372,15 +408,30 @@ __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int
   for (int k = 0; k < steps; ++k) {
 #pragma unroll
     for (int u = 0; u < kSdUnroll; ++u) {
-      uint32_t c[8];
+      // per element pair: v = x + r; code = nearest E2M1 (hardware convert,
+      // same function as e2m1_encode); r = v - value(code), exact.
+      uint32_t pk = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = x[u][i] + r[u][i];
-        c[i] = e2m1_encode(v);
-        r[u][i] = v - e2m1_decode(c[i]);
+      for (int i = 0; i < 4; ++i) {
+        const float v0 = x[u][2 * i] + r[u][2 * i], v1 = x[u][2 * i + 1] + r[u][2 * i + 1];
+        switch (i) {
+          case 0: pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, v0, v1, 1.0f, 0); break;
+          case 1: pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, v0, v1, 1.0f, 1); break;
+          case 2: pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, v0, v1, 1.0f, 2); break;
+          default: pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, v0, v1, 1.0f, 3); break;
+        }
+        float q0, q1;
+        switch (i) {
+          case 0: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0); q0 = q[0]; q1 = q[1]; break; }
+          case 1: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1); q0 = q[0]; q1 = q[1]; break; }
+          case 2: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 2); q0 = q[0]; q1 = q[1]; break; }
+          default: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 3); q0 = q[0]; q1 = q[1]; break; }
+        }
+        r[u][2 * i] = v0 - q0;
+        r[u][2 * i + 1] = v1 - q1;
       }
       if (cidx[u] < n)
-        reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pack8(c);
+        reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pk;
     }
   }
 #pragma unroll
@@ -402,21 +453,25 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_amax_to_cell(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
-                               float* cell, hipStream_t s) {
+                               float* cell, uint8_t* scratch, int64_t scratch_bytes, hipStream_t s) {
   const int64_t cpr = cols / 8, n = rows * cpr;
   const bool contig = (ldx == cols);
-  hipLaunchKernelGGL(k_cell_reset, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(cell));
-  int64_t g = grid_for(n, kThreads * 8);
-  if (g > 2048) g = 2048;
+  int64_t g = grid_for(n, (int64_t)kThreads * kAmaxUnroll * 2);    // ~2 iterations per thread
+  if (g > kAmaxMaxGrid) g = kAmaxMaxGrid;
+  if (g > scratch_bytes / 4) g = scratch_bytes / 4;
   if (g < 1) g = 1;
-  auto* u = reinterpret_cast<uint32_t*>(cell);
+  const int direct = (g == 1);
+  uint32_t* out = direct ? reinterpret_cast<uint32_t*>(cell) : reinterpret_cast<uint32_t*>(scratch);
   if (bf16) {
-    if (contig) hipLaunchKernelGGL((k_amax<true, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
-    else hipLaunchKernelGGL((k_amax<true, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
+    if (contig) hipLaunchKernelGGL((k_amax<true, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, out, direct);
+    else hipLaunchKernelGGL((k_amax<true, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, out, direct);
   } else {
-    if (contig) hipLaunchKernelGGL((k_amax<false, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
-    else hipLaunchKernelGGL((k_amax<false, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, u);
+    if (contig) hipLaunchKernelGGL((k_amax<false, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, out, direct);
+    else hipLaunchKernelGGL((k_amax<false, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, out, direct);
   }
+  if (!direct)
+    hipLaunchKernelGGL(k_amax_finalize, dim3(1), dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(scratch),
+                       (int)g, reinterpret_cast<uint32_t*>(cell));
   return hipGetLastError();
 }
 
@@ -425,7 +480,9 @@ hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t col
                               hipStream_t s) {
   const int dynamic = !ts_is_input;
   if (dynamic) {
-    hipError_t e = launch_amax_to_cell(x, bf16, rows, cols, ldx, ts, s);
+    // the block-scale output doubles as scratch for the partial maxima; the
+    // quantization pass overwrites it afterwards (stream order)
+    hipError_t e = launch_amax_to_cell(x, bf16, rows, cols, ldx, ts, scales, rows * (cols / 16), s);
     if (e != hipSuccess) return e;
   }
   const int64_t cpr = cols / 8, n = rows * cpr;
