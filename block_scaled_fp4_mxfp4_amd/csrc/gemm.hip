@@ -50,8 +50,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 
 inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
-constexpr int BK = 128;           // K elements per stage of the skinny kernel
-constexpr int BKB = BK / 2;       // code bytes per row per stage
 
 // ------------------------------------------------------------ dequant ----
 
@@ -376,146 +374,6 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(const GemmArgs p) {
       }
 }
 
-// ================================================== skinny NVFP4 (M<=16) ====
-//
-// Decode-shaped: the weight is streamed once from HBM, so it is read straight
-// into registers (no LDS staging).  A (<= 16 rows) lives in LDS as codes and
-// E4M3 scales, either copied (pre-quantized) or quantized in the prologue
-// with the recipe of fp4q_quantize_nvfp4 (fused).  Each workgroup owns 64
-// weight rows; its four wavefronts split K and their partial 16 x 64 tiles
-// are summed in a fixed order through LDS, so the fused and unfused entries
-// produce identical Y.
-
-constexpr int SK_MAXK = 7168;   // A codes + scales (9K bytes) within 64 KiB of LDS
-constexpr uint32_t kAmaxFlag = 0x80000000u;
-
-__device__ __forceinline__ float dpp_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-
-template <bool FUSED>
-__global__ __launch_bounds__(kThreads) void k_gemm_nvfp4_skinny(
-    const uint16_t* __restrict__ Abf, int64_t lda, const uint8_t* __restrict__ Ac,
-    const uint8_t* __restrict__ As, float* Ats, int a_dynamic, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const float* __restrict__ Bts, int64_t M, int64_t N, int64_t K,
-    float* __restrict__ Y, int64_t ldy) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* lAc = smem;                          // [16][K/2]
-  uint8_t* lAs = smem + 16 * (K / 2);           // [16][K/16]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
-  const int64_t ldb = K / 2, lds = K / 16;
-
-  float ats;
-  if constexpr (FUSED) {
-    // quantize A[0:M) exactly as k_quant_nvfp4 does; rows >= M become zero
-    const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(Ats));
-    ats = (a_dynamic && (u & kAmaxFlag)) ? __uint_as_float(u & 0x7FFFFFFFu) / 1536.0f : __uint_as_float(u);
-    const float six_st = 6.0f * ats;
-    const int64_t cpr = K / 8, nch = 16 * cpr;
-    for (int64_t c = tid; c < nch; c += kThreads) {
-      const int64_t r = c / cpr, c8 = c - r * cpr;
-      float v[8];
-      if (r < M) {
-        const uint4 q = *reinterpret_cast<const uint4*>(Abf + r * lda + c8 * 8);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(w[i] << 16);
-          v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-      }
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
-      a = fmaxf(a, dpp_xor1(a));
-      uint32_t sb = 0;
-      if (a > 0.0f && ats > 0.0f) sb = e4m3_ceil(a / six_st);
-      const float s = ats * e4m3_decode(sb);
-      const float rho = 1.0f / s;
-      uint32_t p = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p |= ((s == 0.0f) ? 0u : e2m1_encode(v[i] * rho)) << (4 * i);
-      *reinterpret_cast<uint32_t*>(lAc + r * (K / 2) + c8 * 4) = p;
-      if (!(c & 1)) lAs[r * lds + (c8 >> 1)] = (uint8_t)sb;
-    }
-    if (a_dynamic && blockIdx.x == 0 && tid == 0) *Ats = ats;
-  } else {
-    ats = *Ats;
-    const int64_t n16 = 16 * (K / 32);          // 16-byte chunks of A codes
-    for (int64_t c = tid; c < n16; c += kThreads) {
-      const int64_t r = c / (K / 32), cc = c - r * (K / 32);
-      const uint4 q = r < M ? *reinterpret_cast<const uint4*>(Ac + r * (K / 2) + cc * 16) : uint4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<uint4*>(lAc + r * (K / 2) + cc * 16) = q;
-    }
-    for (int64_t c = tid; c < 16 * lds; c += kThreads) {
-      const int64_t r = c / lds;
-      lAs[c] = r < M ? As[r * lds + (c - r * lds)] : (uint8_t)0;
-    }
-  }
-  __syncthreads();
-
-  // this wavefront's share of the K stages
-  const int KT = (int)(K / BK);
-  const int kt0 = (KT * wave) / 4, kt1 = (KT * (wave + 1)) / 4;
-  v4f acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int kt = kt0; kt < kt1; ++kt) {
-    uint4 qb[4];
-    uint32_t wsb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t rn = n0 + j * 16 + r16;
-      if (rn < N) {
-        qb[j] = *reinterpret_cast<const uint4*>(B + rn * ldb + (int64_t)kt * BKB + g * 16);
-        wsb[j] = *reinterpret_cast<const uint16_t*>(Bs + rn * lds + kt * 8 + 2 * g);
-      } else {
-        qb[j] = uint4{0u, 0u, 0u, 0u};
-        wsb[j] = 0u;
-      }
-    }
-    const uint4 qa = *reinterpret_cast<const uint4*>(lAc + r16 * (K / 2) + kt * BKB + g * 16);
-    const uint32_t wsa = *reinterpret_cast<const uint16_t*>(lAs + r16 * lds + kt * 8 + 2 * g);
-    const ScaleSplit xa0 = split_e4m3(wsa & 0xFFu), xa1 = split_e4m3(wsa >> 8);
-    ScaleSplit xb[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xb[j][0] = split_e4m3(wsb[j] & 0xFFu);
-      xb[j][1] = split_e4m3(wsb[j] >> 8);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t wa = s == 0 ? qa.x : s == 1 ? qa.y : s == 2 ? qa.z : qa.w;
-      const v8h ha = dequant8_f16(wa, s < 2 ? xa0 : xa1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t wb = s == 0 ? qb[j].x : s == 1 ? qb[j].y : s == 2 ? qb[j].z : qb[j].w;
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha, dequant8_f16(wb, xb[j][s >> 1]), acc[j], 0, 0, 0);
-      }
-    }
-  }
-  // fixed-order reduction of the four K-partials
-  __syncthreads();                               // A tiles no longer needed
-  float* red = reinterpret_cast<float*>(smem);   // [4][16][64]
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * 16 + g * 4 + r) * 64 + j * 16 + r16] = acc[j][r];
-  __syncthreads();
-  const float tsc = ats * (*Bts);
-  for (int o = tid; o < 16 * 64; o += kThreads) {
-    const int m = o >> 6, n = o & 63;
-    const float v = ((red[(0 * 16 + m) * 64 + n] + red[(1 * 16 + m) * 64 + n]) + red[(2 * 16 + m) * 64 + n]) +
-                    red[(3 * 16 + m) * 64 + n];
-    if (m < M && n0 + n < N) Y[(int64_t)m * ldy + n0 + n] = v * tsc;
-  }
-}
-
 }  // namespace
 
 // Tile shapes (BM, BN, minimum workgroups per CU) of the prefill kernels.
@@ -559,26 +417,6 @@ hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const
                              int64_t ldy, hipStream_t s) {
   GemmArgs p{reinterpret_cast<const uint8_t*>(a), nullptr, nullptr, b, bs, bts, M, N, K, lda, y, ldy, 0, 0};
   return launch_tiled<FMT_W16, FP4Q_W16_TILE>(p, s);
-}
-
-bool skinny_supported(int64_t K) { return K <= SK_MAXK; }
-
-hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8_t* a_codes,
-                                    const uint8_t* a_scales, const float* a_ts, int a_dynamic,
-                                    const uint8_t* b, const uint8_t* bs, const float* bts,
-                                    int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
-                                    hipStream_t s) {
-  size_t a_bytes = 16 * (K / 2) + 16 * (K / 16);
-  const size_t red_bytes = 4 * 16 * 64 * sizeof(float);
-  const size_t shm = a_bytes > red_bytes ? a_bytes : red_bytes;
-  if (a_bf16)
-    hipLaunchKernelGGL((k_gemm_nvfp4_skinny<true>), dim3(cdiv(N, 64)), dim3(kThreads), shm, s,
-                       reinterpret_cast<const uint16_t*>(a_bf16), lda, nullptr, nullptr,
-                       const_cast<float*>(a_ts), a_dynamic, b, bs, bts, M, N, K, y, ldy);
-  else
-    hipLaunchKernelGGL((k_gemm_nvfp4_skinny<false>), dim3(cdiv(N, 64)), dim3(kThreads), shm, s, nullptr,
-                       (int64_t)0, a_codes, a_scales, const_cast<float*>(a_ts), 0, b, bs, bts, M, N, K, y, ldy);
-  return hipGetLastError();
 }
 
 }  // namespace fp4q

@@ -43,14 +43,12 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 enum { FMT_MX = 0, FMT_NV = 1 };
 
-// E4M3 block scale (non-negative byte) -> the same value in fp16, splatted
-// to both halves.  Every E4M3 value is an fp16 normal: (b << 7) + 0x2000
-// re-biases a normal E4M3 exponent (7 -> 15); subnormal E4M3 bytes (< 8)
-// are b * 2^-9.
+// E4M3 block scale (non-negative byte) -> the same value in fp16 (every
+// E4M3 value, subnormals included, is an fp16 normal), splatted to both
+// halves; one hardware fp8 -> fp16 convert.
 __device__ __forceinline__ v2h e4m3_to_h2(uint32_t b) {
-  const uint32_t sub = __builtin_bit_cast(uint16_t, (_Float16)((float)b * 0.001953125f));
-  const uint32_t h = b >= 8u ? (b << 7) + 0x2000u : sub;
-  return __builtin_bit_cast(v2h, h | (h << 16));
+  const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
+  return v2h{t[0], t[0]};
 }
 
 // 8 NVFP4 codes (one dword) -> 8 exact fp16 values code * s_b: the convert

@@ -141,7 +141,7 @@ def test_decode_fused_equals_unfused_and_oracle():
     cw, sw, tw = ONV.quantize(w)
     assert_bytes_equal(host(bc), packed(cw), "decode weight codes")
     Wd = ONV.dequantize(cw, sw, tw)
-    for M in (1, 4, 16):
+    for M in (1, 2, 3, 4, 5, 16):
         xd = dev_bf16(xb[:M])
         y_f, ts_f = L.linear_w4a4(xd, bc, bs, bt)
         ac, as_, at = L.quantize_nvfp4(xd)
@@ -157,6 +157,25 @@ def test_decode_fused_equals_unfused_and_oracle():
         # static activation scale path
         y_s, _ = L.linear_w4a4(xd, bc, bs, bt, a_tscale=at)
         assert_bytes_equal(host(y_s).view(np.uint32), y_f.view(np.uint32), f"static scale M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(77, 384), (33, 7168), (130, 640)])
+def test_decode_ragged(N, K):
+    # ragged output count, short rows (fewer 16-byte chunks than lanes) and
+    # the longest supported row, for every decode batch size
+    L = fp4q()
+    w = synth.normal_f32(250 + N, (N, K), 0.02)
+    x = synth.heavy_tailed_f32(251 + N, 252 + N, (16, K))
+    xb = synth.f32_to_bf16_bits(x)
+    bc, bs, bt = _nv_gpu(dev_f32(w))
+    cw, sw, tw = ONV.quantize(w)
+    for M in (1, 2, 3, 4, 5, 9, 16):
+        yf, tf = L.linear_w4a4(dev_bf16(xb[:M]), bc, bs, bt)
+        ac, as_, at = L.quantize_nvfp4(dev_bf16(xb[:M]))
+        yu = L.gemm_w4a4(L.NVFP4, ac, as_, at, bc, bs, bt)
+        assert_bytes_equal(host(yf).view(np.uint32), host(yu).view(np.uint32), f"fused vs unfused N={N} K={K} M={M}")
+        cx, sx, tx = ONV.quantize(OF.bf16_bits_to_f32(xb[:M]))
+        _check(host(yf), OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), f"decode N={N} K={K} M={M}")
 
 
 def test_gemm_zero_and_one_hot():
@@ -175,3 +194,31 @@ def test_gemm_zero_and_one_hot():
     ce, se, te = ONV.quantize(e)
     y_ref = OG.w4a4_nvfp4(ce, se, te, cw, sw, tw)
     assert np.array_equal(y.astype(np.float64), y_ref.astype(F32).astype(np.float64)) or OG.rel_err(y, y_ref)[0] < 1e-6
+
+
+@pytest.mark.parametrize("M", [3, 40])
+def test_nvfp4_gemm_subnormal_block_scales(M):
+    # blocks far below the tensor maximum get E4M3 block scales in the
+    # subnormal range (scale bytes 0x01..0x07); the GEMMs must dequantize them
+    # exactly
+    K, N = 512, 96
+    rng = np.random.default_rng(240)
+    x = rng.standard_normal((M, K)).astype(F32)
+    x[:, :16] *= 1e5                                   # sets the tensor maximum
+    for j, f in enumerate([1e-1, 3e-2, 1e-2, 3e-3, 1e-3, 3e-4]):
+        x[:, 16 * (j + 1):16 * (j + 2)] *= f
+    w = synth.normal_f32(241, (N, K), 0.02)
+    w[:, 32:48] *= 1e-4
+    L = fp4q()
+    ac, as_, at = _nv_gpu(dev_f32(x))
+    bc, bs, bt = _nv_gpu(dev_f32(w))
+    cx, sx, tx = ONV.quantize(x)
+    cw, sw, tw = ONV.quantize(w)
+    assert (sx[:, 1:7] < 8).any() and (sx[:, 1:7] > 0).any()       # subnormal scales present
+    y = host(L.gemm_w4a4(L.NVFP4, ac, as_, at, bc, bs, bt))
+    _check(y, OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), f"nvfp4 subnormal scales M={M}")
+    if M <= 16:
+        xb = synth.f32_to_bf16_bits(x)
+        yf, _ = L.linear_w4a4(dev_bf16(xb), bc, bs, bt)
+        cxb, sxb, txb = ONV.quantize(OF.bf16_bits_to_f32(xb))
+        _check(host(yf), OG.w4a4_nvfp4(cxb, sxb, txb, cw, sw, tw), f"decode subnormal scales M={M}")
