@@ -242,9 +242,6 @@ int fp4q_linear_w4a4(const void* a_bf16, int64_t lda, float* a_tscale, int a_tsc
   if ((reinterpret_cast<uintptr_t>(y) & 3u)) return fail(FP4Q_ERR_BAD_ALIGN, "y must be 4-byte aligned");
   if (int st = check_device()) return st;
   hipStream_t s = as_stream(stream);
-  if (!a_tscale_is_input) {
-    if (int st = launch_status(fp4q::launch_amax_to_cell(a_bf16, 1, M, K, lda, a_tscale, nullptr, 0, s), "linear_w4a4 amax")) return st;
-  }
   return launch_status(fp4q::launch_gemm_nvfp4_skinny(a_bf16, lda, nullptr, nullptr, a_tscale, !a_tscale_is_input,
                                                       b_codes, b_scales, b_tscale, M, N, K, y, ldy, s),
                        "linear_w4a4");

@@ -3,25 +3,26 @@
 // ("Why Gated DeltaNet Survives 4-Bit Quantization", limitations: decode was
 // slowed by the separate small-batch NVFP4 activation-quantization kernel).
 //
-// The weight (N x K NVFP4, ~50 MB for 17408 x 5120) is read exactly once,
-// so the kernel is an HBM stream with as little VALU work per weight byte as
-// possible:
-//  * a workgroup owns 64 weight rows; its four wavefronts are two row
-//    groups (32 rows = two 16-row fragments each, so every dequantized
-//    activation fragment feeds two matrix instructions) times two K halves;
-//    the two K-half partials are summed in a fixed order through LDS, so the
-//    fused and the pre-quantized entry points produce identical Y;
-//  * the weight codes and E4M3 scales of the next PF stages (128 K elements
-//    each) are in flight in registers while the current ones are consumed,
-//    and the first group is issued before the activation prologue;
-//  * the <= 16 activation rows live in LDS as NVFP4 codes + scales with
-//    padded row strides (conflict-free fragment reads); the prologue copies
-//    or quantizes (exactly the fp4q_quantize_nvfp4 recipe) only the M real
-//    rows and zero-fills the rest;
-//  * both operands are dequantized exactly to fp16 in registers
-//    (code * s_b has at most 6 significant bits); E4M3 scales become fp16
-//    with one v_cvt_scalef32_pk_f16_fp8 per two blocks; the fp16 matrix core
-//    multiplies and the tensor scales are applied once at the end.
+// The weight (N x K NVFP4, ~50 MB for 17408 x 5120) is read exactly once, so
+// each form is an HBM stream with as little work per weight byte as
+// possible.  Three forms, picked by shape:
+//  * M = 1: row streaming (k_decode_rows) -- each wavefront walks whole
+//    weight rows with coalesced 1 KiB loads and v_dot2 against the
+//    activation held as exact fp16 in LDS;
+//  * 2 <= M <= 16, K <= 5120, K % 256 == 0: the streamed form
+//    (k_decode_stream) -- 16-row weight groups pulled whole into LDS by
+//    direct global->LDS loads, sixteen wavefronts splitting K on the fp16
+//    matrix core with register-resident activation fragments;
+//  * other shapes: the register-staged form (k_decode) -- 64 weight rows per
+//    workgroup, K streamed through registers.
+// Every form dequantizes both operands exactly to fp16 (code * s_b has at
+// most 6 significant bits), accumulates in fp32, adds partial sums in a
+// fixed order (so the fused and the pre-quantized entry points agree bit for
+// bit) and applies the two tensor scales once at the end.  The fused
+// prologues quantize with exactly the fp4q_quantize_nvfp4 recipe; with a
+// dynamic activation scale the rows and streamed forms derive it from the
+// exact amax in every workgroup (max is order-free), the register-staged
+// form reads it from a separate amax pass.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -284,6 +285,74 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   }
 }
 
+// Quantizes the M x K bf16 activation rows with the NVFP4 recipe of
+// fp4q_quantize_nvfp4, using all NT threads of the workgroup: every thread
+// loads its (at most U) 8-element chunks once (chunk c: row c / (K / 8),
+// elements [8 (c % (K / 8)), +8)); with `dynamic` the tensor scale is
+// fl(amax / 1536) over the whole activation (max is exact, so every
+// workgroup derives the same value), else ats_in.  Lane pairs share a
+// 16-block (DPP); put(r, c8, codes, scale) stores one chunk's four code
+// bytes and, on even c8, the block scale.  Returns the tensor scale.
+template <int NT, int U, typename Put>
+__device__ __forceinline__ float quantize_act_block(const uint16_t* __restrict__ A, int64_t lda, int M, int K,
+                                                    float ats_in, bool dynamic, float* red, Put put) {
+  const int tid = threadIdx.x, cpr = K / 8, nch = M * cpr;
+  uint4 q[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = tid + u * NT;
+    const int cc = c < nch ? c : 0;                        // chunk 0 is real data: harmless to the max
+    q[u] = *reinterpret_cast<const uint4*>(A + (int64_t)(cc / cpr) * lda + (cc % cpr) * 8);
+  }
+  float ats = ats_in;
+  if (dynamic) {
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a = fmaxf(a, fmaxf(__builtin_fabsf(__uint_as_float(w[i] << 16)), __builtin_fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) t = fmaxf(t, red[w]);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    ats = t / 1536.0f;
+  }
+  const float six_st = 6.0f * ats;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = tid + u * NT;
+    const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+    a = fmaxf(a, dpp_xor1(a));                             // cpr is even: pairs share a row
+    uint32_t sb = 0;
+    if (a > 0.0f && ats > 0.0f) sb = e4m3_ceil(a / six_st);
+    const float sc = ats * e4m3_decode(sb);
+    const float rho = 1.0f / sc;
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0] * rho, v[1] * rho, 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2] * rho, v[3] * rho, 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4] * rho, v[5] * rho, 1.0f, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6] * rho, v[7] * rho, 1.0f, 3);
+    if (c < nch) put(c / cpr, c % cpr, (sc == 0.0f) ? 0u : p, sb);
+  }
+  return ats;
+}
+
 // ------------------------------------------------------------ M <= 4 ----
 //
 // Row-streaming form for the smallest batches: each wavefront walks whole
@@ -367,39 +436,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_rows(
     *reinterpret_cast<uint4*>(lA + r * Ki + c8 * 8) = o;
   };
   const int cpr = Ki / 8, nch = Mi * cpr;
+  __shared__ float red_amax[kThreads / 64];
   if constexpr (FUSED) {
-    // quantize A[0:M) exactly as k_quant_nvfp4 does (one lane per 8 values,
-    // lane pairs share a 16-block)
-    const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(Ats));
-    ats = (a_dynamic && (u & kAmaxFlag)) ? __uint_as_float(u & 0x7FFFFFFFu) / 1536.0f : __uint_as_float(u);
-    const float six_st = 6.0f * ats;
-    const int nch_pad = (nch + kThreads - 1) / kThreads * kThreads;   // all lanes join the DPP
-    for (int c = tid; c < nch_pad; c += kThreads) {
-      const bool in = c < nch;
-      const int r = in ? c / cpr : 0, c8 = in ? c % cpr : 0;
-      const uint4 q = *reinterpret_cast<const uint4*>(Abf + (int64_t)r * lda + c8 * 8);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
-      a = fmaxf(a, dpp_xor1(a));
-      uint32_t sb = 0;
-      if (a > 0.0f && ats > 0.0f) sb = e4m3_ceil(a / six_st);
-      const float sc = ats * e4m3_decode(sb);
-      const float rho = 1.0f / sc;
-      uint32_t p = 0;
-      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0] * rho, v[1] * rho, 1.0f, 0);
-      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2] * rho, v[3] * rho, 1.0f, 1);
-      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4] * rho, v[5] * rho, 1.0f, 2);
-      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6] * rho, v[7] * rho, 1.0f, 3);
-      if (in) put8(r, c8, (sc == 0.0f) ? 0u : p, sb);
-    }
+    ats = quantize_act_block<kThreads, 4 * MM>(Abf, lda, Mi, Ki, *Ats, a_dynamic != 0, red_amax,
+                                               [&](int r, int c8, uint32_t p, uint32_t sb) { put8(r, c8, p, sb); });
     if (a_dynamic && blockIdx.x == 0 && tid == 0) *Ats = ats;
   } else {
     ats = *Ats;
@@ -499,40 +539,327 @@ hipError_t launch_rows(int ch, unsigned grid, size_t shm, hipStream_t s, const u
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- streamed form ----
+//
+// A workgroup owns a contiguous range of weight rows and walks it in 16-row
+// groups.  Each group (16 rows x K: 40 KiB of codes + 5 KiB of scales at
+// K = 5120) is pulled into LDS whole, by direct global->LDS loads issued back
+// to back, so at any moment the chip reads a contiguous window of the weight
+// rather than a thin K-slice of every row; two group buffers alternate.  The
+// loads are placed in matrix-fragment order (load j, lane l: row l % 16,
+// bytes 64 j + 16 (l / 16)), so every fragment read is one linear,
+// conflict-free 16-byte LDS access.
+//
+// Sixteen wavefronts split K: wavefront w owns at most three 128-K steps, for
+// which it holds the activation fragments already dequantized to fp16 in
+// registers for the whole kernel, so per weight group it only dequantizes
+// weight codes and runs the fp16 matrix core.  The sixteen partial tiles are
+// summed in a fixed order through LDS by wavefronts 0-3, which also write the
+// outputs; wavefronts 4-15 issue every direct load and wait on them with
+// explicit vector-memory counts.  Scale bytes travel in 16-byte chunks: load j, lane l
+// moves chunk (l / 16) + 4 j of row l % 16's scales.
+constexpr int kStThreads = 1024;
+constexpr int kStWaves = kStThreads / 64;
+constexpr int kStMaxKT = 40;             // three group buffers + partial tiles within 160 KiB; K <= 5120
+constexpr int kStKW = 3;                 // max 128-K steps per wavefront (ceil(40 / 16))
+constexpr int kStNB = 3;                 // group buffers
+// activation chunks per thread in the fused prologue: 8 x 5120 / 8 / 1024
+// = 5 (M <= 8) and 16 x 5120 / 8 / 1024 = 10 (M <= 16)
+
+// LDS: three group buffers of (KT + SJ) KiB, the third of which first holds
+// the activation image (same layout, read once in the prologue), then the
+// 16 wavefronts' partial tiles (16 x 4 x 64 floats).
+struct StLayout {
+  int KT, SJ;                            // 128-K steps; 1 KiB scale loads per group
+  int buf, a_c, a_s, red, total;         // buf: bytes per group buffer
+};
+__host__ __device__ inline StLayout st_layout(int K) {
+  StLayout L;
+  L.KT = K / 128;
+  L.SJ = (L.KT + 7) / 8;
+  L.buf = (L.KT + L.SJ) * 1024;
+  L.a_c = 2 * L.buf;
+  L.a_s = 2 * L.buf + L.KT * 1024;
+  L.red = 3 * L.buf;
+  L.total = L.red + kStWaves * 4 * 64 * 4;
+  return L;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p);
+}
+// one direct global->LDS load of 16 bytes per lane; lane l's bytes land at
+// lds_base + 16 l.  No registers are written; completion is tracked by the
+// explicit vector-memory waits below.
+__device__ __forceinline__ void st_dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define FP4Q_VMW(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+  switch (n) {
+    FP4Q_VMW(1) FP4Q_VMW(2) FP4Q_VMW(3) FP4Q_VMW(4) FP4Q_VMW(5) FP4Q_VMW(6) FP4Q_VMW(7) FP4Q_VMW(8)
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+#undef FP4Q_VMW
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool FUSED, int ACTU>
+__global__ __launch_bounds__(kStThreads) void k_decode_stream(
+    const uint16_t* __restrict__ Abf, int64_t lda, const uint8_t* __restrict__ Ac,
+    const uint8_t* __restrict__ As, float* Ats, int a_dynamic, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const float* __restrict__ Bts, int M, int N, int K, int rows_per_wg,
+    float* __restrict__ Y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const StLayout L = st_layout(K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int KT = L.KT, SJ = L.SJ, nsc = KT / 2;           // 16-byte scale chunks per row
+  const uint32_t ldb = (uint32_t)K / 2, lds = (uint32_t)K / 16;
+  const int row0 = blockIdx.x * rows_per_wg;
+  const int row_end = min(N, row0 + rows_per_wg);
+  const int G = (row_end - row0 + 15) / 16;
+  const uint32_t sbase = lds_addr(smem);
+  // scalars first: a later plain load would wait behind the direct loads
+  const float bts = *Bts;
+  const float ats_in = *Ats;
+
+  // direct loads of one 16-row group into buffer s (wavefronts 4-15, which
+  // issue no other vector-memory operation inside the loop, so their explicit
+  // wait counts are exact; rows past the range re-read the last row, so every
+  // lane of every load is active and the per-wavefront load count is the
+  // same for every group)
+  constexpr int kFirstDma = 4;
+  const bool dma_wave = wave >= kFirstDma;
+  const int dw = wave - kFirstDma, nd = kStWaves - kFirstDma;
+  const int js0 = ((dw - KT) % nd + nd) % nd;             // first scale load of this wavefront
+  auto issue_group = [&](int gi, int s) {
+    const int r = min(row0 + gi * 16 + r16, row_end - 1);
+    const uint32_t oc = (uint32_t)r * ldb + (uint32_t)g * 16u;
+    const uint32_t os = (uint32_t)r * lds;
+    const uint32_t bc = sbase + (uint32_t)(s * L.buf), bsc = bc + (uint32_t)(KT * 1024);
+    for (int j = dw; j < KT; j += nd) st_dma16(B, oc + (uint32_t)j * 64u, bc + (uint32_t)j * 1024u);
+    for (int j = js0; j < SJ; j += nd)
+      st_dma16(Bs, os + (uint32_t)min(g + 4 * j, nsc - 1) * 16u, bsc + (uint32_t)j * 1024u);
+  };
+  int cnt = 0;
+  if (dma_wave) {
+    for (int j = dw; j < KT; j += nd) ++cnt;
+    for (int j = js0; j < SJ; j += nd) ++cnt;
+  }
+
+  float ats;
+  if constexpr (!FUSED) {
+    if (dma_wave) {
+      // activation codes and scales by the same direct loads (rows >= M
+      // re-read row M - 1; their outputs are never stored)
+      const int r = min(r16, M - 1);
+      for (int j = dw; j < KT; j += nd)
+        st_dma16(Ac, (uint32_t)r * ldb + (uint32_t)g * 16u + (uint32_t)j * 64u, sbase + (uint32_t)L.a_c + (uint32_t)j * 1024u);
+      for (int j = js0; j < SJ; j += nd)
+        st_dma16(As, (uint32_t)r * lds + (uint32_t)min(g + 4 * j, nsc - 1) * 16u, sbase + (uint32_t)L.a_s + (uint32_t)j * 1024u);
+    }
+    // every activation load is queued before any weight load: the vector
+    // memory path returns in order, and the (cached) activation must not wait
+    // behind the weight stream
+    __builtin_amdgcn_s_barrier();
+    if (dma_wave) {
+      issue_group(0, 0);
+      if (G > 1) issue_group(1, 1);
+      wait_vmcnt(G > 1 ? 2 * cnt : cnt);                   // activation image complete
+    }
+    ats = ats_in;
+  } else {
+    // rows >= M of the image are zero
+    for (int sl = tid; sl < KT * 64; sl += kStThreads)
+      if ((sl & 15) >= M) *reinterpret_cast<uint4*>(smem + L.a_c + sl * 16) = uint4{0u, 0u, 0u, 0u};
+    for (int sl = tid; sl < SJ * 64; sl += kStThreads)
+      if ((sl & 15) >= M) *reinterpret_cast<uint4*>(smem + L.a_s + sl * 16) = uint4{0u, 0u, 0u, 0u};
+    ats = quantize_act_block<kStThreads, ACTU>(
+        Abf, lda, M, K, ats_in, a_dynamic != 0, reinterpret_cast<float*>(smem + L.red),
+        [&](int r, int c8, uint32_t p, uint32_t sb) {
+          const int kt = c8 >> 4, k8 = c8 & 15;
+          *reinterpret_cast<uint32_t*>(smem + L.a_c + kt * 1024 + (((k8 >> 2) << 4) + r) * 16 + (k8 & 3) * 4) = p;
+          if (!(c8 & 1)) {
+            const int b = c8 >> 1, ch = b >> 4;
+            smem[L.a_s + (ch >> 2) * 1024 + (((ch & 3) << 4) + r) * 16 + (b & 15)] = (uint8_t)sb;
+          }
+        });
+    if (a_dynamic && blockIdx.x == 0 && tid == 0) *Ats = ats;
+    // the weight stream starts once the activation loads have returned (the
+    // vector memory path returns in order, and a plain load waits for every
+    // earlier load of its wavefront)
+    if (dma_wave) {
+      issue_group(0, 0);
+      if (G > 1) issue_group(1, 1);
+    }
+  }
+  lds_barrier();                                           // activation image complete
+
+  // this wavefront's activation fragments, dequantized once
+  const int kb = (wave * KT) / kStWaves, ke = ((wave + 1) * KT) / kStWaves;
+  v8h ah[kStKW][4];
+#pragma unroll
+  for (int i = 0; i < kStKW; ++i) {
+    const int kt = min(kb + i, KT - 1);
+    const uint4 qa = *reinterpret_cast<const uint4*>(smem + L.a_c + kt * 1024 + lane * 16);
+    const int c = kt >> 1;
+    const int so = (c >> 2) * 1024 + (((c & 3) << 4) + r16) * 16 + ((kt & 1) << 3) + 2 * g;
+    v2h sa0, sa1;
+    e4m3x2_to_h2(*reinterpret_cast<const uint16_t*>(smem + L.a_s + so), sa0, sa1);
+    ah[i][0] = dequant8(qa.x, sa0);
+    ah[i][1] = dequant8(qa.y, sa0);
+    ah[i][2] = dequant8(qa.z, sa1);
+    ah[i][3] = dequant8(qa.w, sa1);
+  }
+  lds_barrier();                                           // the image's space becomes buffer 2
+  if (dma_wave && G > 2) issue_group(2, 2);
+  const float tsc = ats * bts;
+
+  float* red = reinterpret_cast<float*>(smem + L.red);
+  for (int gi = 0; gi < G; ++gi) {
+    const int s = gi % kStNB;
+    if (dma_wave) wait_vmcnt(min(G - 1 - gi, kStNB - 1) * cnt);   // groups after gi stay in flight
+    lds_barrier();                                         // group gi in LDS
+
+    // copy this wavefront's slice of the group to registers, so the buffer
+    // can be refilled before the matrix work starts
+    const uint8_t* bcode = smem + s * L.buf;
+    const uint8_t* bscl = bcode + KT * 1024;
+    uint4 qb[kStKW];
+    uint32_t wsb[kStKW];
+#pragma unroll
+    for (int i = 0; i < kStKW; ++i) {
+      const int kt = min(kb + i, KT - 1);
+      qb[i] = *reinterpret_cast<const uint4*>(bcode + kt * 1024 + lane * 16);
+      const int c = kt >> 1;
+      wsb[i] = *reinterpret_cast<const uint16_t*>(bscl + (c >> 2) * 1024 + (((c & 3) << 4) + r16) * 16 +
+                                                  ((kt & 1) << 3) + 2 * g);
+    }
+    lds_barrier();                                         // buffer s free
+    if (dma_wave && gi + kStNB < G) issue_group(gi + kStNB, s);
+
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kStKW; ++i) {
+      if (kb + i < ke) {
+        v2h sb0, sb1;
+        e4m3x2_to_h2(wsb[i], sb0, sb1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i][0], dequant8(qb[i].x, sb0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i][1], dequant8(qb[i].y, sb0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i][2], dequant8(qb[i].z, sb1), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i][3], dequant8(qb[i].w, sb1), acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+    lds_barrier();                                         // partials in LDS
+    if (tid < 256) {
+      // thread t sums output (r, l) = (t / 64, t % 64) of the tile over the
+      // 16 wavefronts in order; lane l of a tile holds column l % 16 and
+      // row 4 (l / 16) + r
+      const int r = tid >> 6;
+      float v = red[r * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < kStWaves; ++w) v = v + red[(w * 4 + r) * 64 + lane];
+      const int nrow = min(16, row_end - (row0 + gi * 16));
+      const int m = g * 4 + r;
+      if (m < M && r16 < nrow) Y[m * ldy + row0 + gi * 16 + r16] = v * tsc;
+    }
+  }
+}
+
 inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
 bool skinny_supported(int64_t K) { return K <= SK_MAXK; }
 
+bool stream_supported(int64_t N, int64_t K) {
+  return K % 256 == 0 && K / 128 <= kStMaxKT && N * (K / 2) < (int64_t(1) << 32);
+}
+
+#ifndef FP4Q_DEC_ROWS_MAXM
+#define FP4Q_DEC_ROWS_MAXM 1
+#endif
+
+// a_dynamic (fused form only): the activation tensor scale is computed from
+// the activation's amax and written to a_ts.
 hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8_t* a_codes,
                                     const uint8_t* a_scales, const float* a_ts, int a_dynamic,
                                     const uint8_t* b, const uint8_t* bs, const float* bts,
                                     int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
                                     hipStream_t s) {
+  float* ats = const_cast<float*>(a_ts);
+  const bool fused = a_bf16 != nullptr;
+  if (M > FP4Q_DEC_ROWS_MAXM && stream_supported(N, K)) {
+    const StLayout L = st_layout((int)K);
+    // spread the rows evenly over one workgroup per compute unit
+    static int n_cu = 0;
+    if (!n_cu) {
+      int dev = 0, v = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        n_cu = v;
+      else
+        n_cu = 256;
+    }
+    const int64_t groups = (N + 15) / 16;
+    int64_t grid = groups < n_cu ? groups : n_cu;
+    const int64_t rpw = (N + grid - 1) / grid;
+    grid = (N + rpw - 1) / rpw;
+    // allow the full 160 KiB of LDS once per process
+    static hipError_t attr = [] {
+      const void* ks[3] = {reinterpret_cast<const void*>(&k_decode_stream<false, 1>),
+                           reinterpret_cast<const void*>(&k_decode_stream<true, 5>),
+                           reinterpret_cast<const void*>(&k_decode_stream<true, 10>)};
+      for (const void* k : ks) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }();
+    if (attr != hipSuccess) return attr;
+    auto launch = [&](auto kern) -> hipError_t {
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kStThreads), (size_t)L.total, s,
+                         reinterpret_cast<const uint16_t*>(a_bf16), lda, a_codes, a_scales, ats,
+                         fused ? a_dynamic : 0, b, bs, bts, (int)M, (int)N, (int)K, (int)rpw, y, ldy);
+      return hipGetLastError();
+    };
+    if (!fused) return launch(&k_decode_stream<false, 1>);
+    if (M <= 8) return launch(&k_decode_stream<true, 5>);
+    return launch(&k_decode_stream<true, 10>);
+  }
   if (M <= kRowsMaxM) {
     // at most four 16-byte chunks per lane: K / 32 <= 256 holds for K <= 7168
     const int ch = (int)((K / 32 + 63) / 64);
     const size_t shm_r = (size_t)M * K * 2;
     const unsigned grid = FP4Q_ROWS_GRID;
-    if (a_bf16)
+    if (fused)
       return launch_rows<true>(ch, grid, shm_r, s, reinterpret_cast<const uint16_t*>(a_bf16), lda, nullptr,
-                               nullptr, const_cast<float*>(a_ts), a_dynamic, b, bs, bts, M, N, K, y, ldy);
-    return launch_rows<false>(ch, grid, shm_r, s, nullptr, (int64_t)0, a_codes, a_scales,
-                              const_cast<float*>(a_ts), 0, b, bs, bts, M, N, K, y, ldy);
+                               nullptr, ats, a_dynamic, b, bs, bts, M, N, K, y, ldy);
+    return launch_rows<false>(ch, grid, shm_r, s, nullptr, (int64_t)0, a_codes, a_scales, ats, 0, b, bs, bts, M,
+                              N, K, y, ldy);
+  }
+  if (fused && a_dynamic) {
+    // this form reads the amax from the tensor-scale cell
+    const hipError_t e = launch_amax_to_cell(a_bf16, 1, M, K, lda, ats, nullptr, 0, s);
+    if (e != hipSuccess) return e;
   }
   // the activation tiles, and afterwards the K-half reduction buffer
   // (2 row groups x FRAGS x 4 x 64 floats), share the allocation
   const size_t shm_tiles = 16 * (K / 2 + 16) + 16 * (K / 16 + 4);
   const size_t shm_red = 2 * FRAGS * 4 * 64 * sizeof(float);
   const size_t shm = shm_tiles > shm_red ? shm_tiles : shm_red;
-  if (a_bf16)
+  if (fused)
     hipLaunchKernelGGL((k_decode<true>), dim3(cdiv(N, RPG)), dim3(kThreads), shm, s,
-                       reinterpret_cast<const uint16_t*>(a_bf16), lda, nullptr, nullptr,
-                       const_cast<float*>(a_ts), a_dynamic, b, bs, bts, M, N, K, y, ldy);
+                       reinterpret_cast<const uint16_t*>(a_bf16), lda, nullptr, nullptr, ats, a_dynamic, b, bs,
+                       bts, M, N, K, y, ldy);
   else
     hipLaunchKernelGGL((k_decode<false>), dim3(cdiv(N, RPG)), dim3(kThreads), shm, s, nullptr, (int64_t)0,
-                       a_codes, a_scales, const_cast<float*>(a_ts), 0, b, bs, bts, M, N, K, y, ldy);
+                       a_codes, a_scales, ats, 0, b, bs, bts, M, N, K, y, ldy);
   return hipGetLastError();
 }
 

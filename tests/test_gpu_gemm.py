@@ -159,10 +159,11 @@ def test_decode_fused_equals_unfused_and_oracle():
         assert_bytes_equal(host(y_s).view(np.uint32), y_f.view(np.uint32), f"static scale M={M}")
 
 
-@pytest.mark.parametrize("N,K", [(77, 384), (33, 7168), (130, 640)])
+@pytest.mark.parametrize("N,K", [(77, 384), (33, 7168), (130, 640), (1000, 512), (4100, 5120), (300, 2560)])
 def test_decode_ragged(N, K):
-    # ragged output count, short rows (fewer 16-byte chunks than lanes) and
-    # the longest supported row, for every decode batch size
+    # ragged output count, short rows (fewer 16-byte chunks than lanes), the
+    # longest supported row, and for the streamed form: row ranges that end
+    # inside a 16-row group, its largest K (5120) and uneven load splits
     L = fp4q()
     w = synth.normal_f32(250 + N, (N, K), 0.02)
     x = synth.heavy_tailed_f32(251 + N, 252 + N, (16, K))
