@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy (HBM byte-counter calibration)")
     return p.parse_args()
 
 
@@ -56,12 +58,23 @@ def main():
 
     import numpy as np
     import torch
-    from block_scaled_fp4_mxfp4_amd import fp4q as L, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        # 1 GiB read + 1 GiB written per launch: the reference for FETCH_SIZE / WRITE_SIZE
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "launches": 3}), flush=True)
+        return
+
+    from block_scaled_fp4_mxfp4_amd import fp4q as L, synth
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -133,7 +146,8 @@ def main():
 
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK["fp16_TFLOPs"],
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK["fp16_TFLOPs"], 4), "traffic": traffic,
-                "kernel": "k_gemm_nvfp4 (fp16 MFMA on exact NVFP4 dequant)",
+                "kernel": "k_gemm_mx3<FMT_NV, 256, 160, 64> (LDS-DMA tiles, exact NVFP4 dequant, fp16 MFMA)",
+                "algorithmic": "2*M*N*K flop per launch (M=4096, N=10240, K=5120)",
                 "frac_of_fp4_peak": round(gemm_tflops / PEAK["fp4_TFLOPs"], 4)}
 
     out = {
@@ -165,7 +179,7 @@ def main():
 
 def _kernel_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "codec.h"):
+    for f in ("gemm_mx.hip", "codec.h"):
         with open(os.path.join(ROOT, "block_scaled_fp4_mxfp4_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
