@@ -84,7 +84,10 @@ const char* fp4q_last_error(void);
  *          16-byte aligned, ldx*sizeof(elem) a multiple of 16, ldx >= cols.
  * cols:    multiple of 16.
  * codes:   [rows][cols/2] bytes, 16-byte aligned (output).
- * scales:  [rows][cols/16] E4M3 bytes (output).
+ * scales:  [rows][cols/16] E4M3 bytes (output).  With
+ *          tensor_scale_is_input == 0 the call first uses this buffer as
+ *          scratch for per-workgroup partial maxima (no allocation), then
+ *          overwrites it with the block scales.
  * tensor_scale: one fp32.  tensor_scale_is_input == 0: the library computes
  *          A over the whole tensor on the stream and writes s_t here (the
  *          location is also used as the reduction cell while the call runs);
@@ -213,7 +216,10 @@ int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda,
  * Y is bit-identical to fp4q_quantize_nvfp4 followed by fp4q_gemm_w4a4.
  * M in [1, 16]; K a multiple of 128 and at most 7168 (A is held on chip).
  * a_tscale: one fp32, same in/out rule as fp4q_quantize_nvfp4's
- * tensor_scale.
+ * tensor_scale (with a_tscale_is_input == 0 every workgroup derives s_t
+ * from the exact amax of A, so s_t equals fp4q_quantize_nvfp4's).
+ * lda: row stride of a in elements, a multiple of 8, >= K; a 16-byte
+ * aligned.  b_scales 8-byte aligned; y [M][ldy] fp32, ldy >= N.
  */
 int fp4q_linear_w4a4(const void* a_bf16, int64_t lda, float* a_tscale, int a_tscale_is_input,
                      const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
