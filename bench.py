@@ -30,6 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+WARM_S = 0.3          # minimum seconds of untimed warm-up before any timed region
 PEAK = {"hbm_GBps": 8000.0, "fp4_TFLOPs": 10100.0, "fp8_TFLOPs": 5000.0, "fp16_TFLOPs": 2500.0,
         "bf16_TFLOPs": 2500.0}
 
@@ -112,9 +113,17 @@ def main():
         if record is not None:
             record[3].record(stream)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    # W untimed warmup steps, continued (untimed) until the GPU has run the
+    # step for WARM_S seconds: MI355X ramps its clocks over the first ~10 ms
+    # of sustained matrix work, and a cold GEMM runs ~20% slower.
+    log(f"warmup {args.warmup} steps (+ until {WARM_S} s of warm-up)")
+    tw = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - tw < WARM_S:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     recs = [[ev() for _ in range(4)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
@@ -154,7 +163,7 @@ def main():
         "metric": "W4A4 FP4 GEMM TFLOP/s + quantizer GB/s, fraction of MI355X roofline",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4 (e2m1+e4m3, fp16 mfma, fp32 acc)",
+        "scaling": "weak", "vs_baseline": None, "warmup_steps_run": n_warm, "dtype": "nvfp4 (e2m1+e4m3, fp16 mfma, fp32 acc)",
         "data": "synthetic (seeded heavy-tailed activations, N(0,0.02^2) weights)",
         "config": {"workload": "nvfp4_prefill X[4096x5120] W[10240x5120] bf16 -> quantize both -> GEMM",
                    "M": M, "N": N, "K": K, "parallelism": "single GPU"},
@@ -188,8 +197,13 @@ def _kernel_hash():
 # ---------------------------------------------------------------- extras ----
 
 def _time_op(torch, stream, fn, iters, warm=3):
-    for _ in range(warm):
-        fn(0)
+    t0 = time.perf_counter()
+    n = 0
+    while n < warm or time.perf_counter() - t0 < 0.05:   # >= 50 ms of warm-up per operation
+        fn(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(evs):

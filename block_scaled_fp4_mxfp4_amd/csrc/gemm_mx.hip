@@ -6,10 +6,10 @@
 // the OCP MXFP4 tensors feed the instruction as stored: no dequantization.
 //
 // Data movement (the part that decides speed here):
-//  * a 256-thread workgroup owns a BM x BN tile (256 x 224 or 256 x 256);
-//    its four wavefronts own 128 x BN/2 each, i.e. 8 x (BN/32) 16 x 16
-//    accumulator tiles, so every 16-byte fragment read from LDS feeds BN/32
-//    or 8 matrix instructions;
+//  * a 512-thread workgroup owns a BM x BN tile (256 x 224 or 256 x 256);
+//    its eight wavefronts (two per SIMD, so one wave's dequantization or
+//    LDS reads overlap the other's matrix instructions) own 64 x BN/2 each,
+//    i.e. 4 x (BN/32) 16 x 16 accumulator tiles;
 //  * K advances 256 elements (one whole 128-byte line of codes per row) per
 //    stage through a two-slot LDS ring filled by direct global->LDS loads
 //    (global_load_lds, 16 bytes per lane) issued one stage ahead, so no
@@ -31,6 +31,10 @@
 #include <stdint.h>
 
 #include "internal.h"
+
+#ifndef FP4Q_NV_SCHED_SPLIT
+#define FP4Q_NV_SCHED_SPLIT 0   // 1: one scheduling region per 16-element block half
+#endif
 
 namespace fp4q {
 
@@ -62,8 +66,18 @@ __device__ __forceinline__ v8h dequant8(uint32_t w, v2h sb) {
   return __builtin_bit_cast(v8h, uint4{o0, o1, o2, o3});
 }
 
-constexpr int kThreads = 256;
-constexpr int NS = 2;         // LDS ring slots
+// vmcnt(n) for a wave-uniform n in [0, 31] (the count must be an immediate)
+__device__ __forceinline__ void wait_vm(int n) {
+#define FP4Q_VMW(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+  switch (n) {
+    FP4Q_VMW(1) FP4Q_VMW(2) FP4Q_VMW(3) FP4Q_VMW(4) FP4Q_VMW(5) FP4Q_VMW(6) FP4Q_VMW(7) FP4Q_VMW(8)
+    FP4Q_VMW(9) FP4Q_VMW(10) FP4Q_VMW(11) FP4Q_VMW(12) FP4Q_VMW(13) FP4Q_VMW(14) FP4Q_VMW(15) FP4Q_VMW(16)
+    FP4Q_VMW(17) FP4Q_VMW(18) FP4Q_VMW(19) FP4Q_VMW(20) FP4Q_VMW(21) FP4Q_VMW(22) FP4Q_VMW(23) FP4Q_VMW(24)
+    FP4Q_VMW(25) FP4Q_VMW(26) FP4Q_VMW(27) FP4Q_VMW(28) FP4Q_VMW(29) FP4Q_VMW(30) FP4Q_VMW(31)
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+#undef FP4Q_VMW
+}
 
 struct MxArgs {
   const uint8_t* A;
@@ -123,34 +137,43 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
                :: "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(off), "s"(base) : "memory");
 }
 
-template <int FMT, int BM, int BN, int CB>
+// LDS stage layout and direct-load plan of one K stage for NT threads.  Each
+// operand is a list of 16-byte (codes) or 4-byte (scales) units; unit s is
+// loaded by thread s % NT in its load s / NT, and whole 64-unit groups
+// belong to one wavefront, so "is this load present" is wave-uniform.
+template <int FMT, int BM, int BN, int CB, int NT>
 struct MxLayout {
-  static constexpr int B_ROWS = ((BN + 63) / 64) * 64;   // whole 64-row load instructions
+  static constexpr int B_ROWS = BN;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = A_OFF + BM * CB;
   static constexpr int SA_OFF = B_OFF + B_ROWS * CB;
   static constexpr int SCB = FMT == FMT_MX ? CB / 16 : CB / 8;  // scale bytes per row per stage
   static constexpr int SB_OFF = SA_OFF + BM * SCB;
   static constexpr int STAGE = SB_OFF + B_ROWS * SCB;
-  static constexpr int A_LD = BM * CB / 16 / kThreads;        // 16-byte loads per thread
-  static constexpr int B_LD = B_ROWS * CB / 16 / kThreads;
-  static constexpr int SA_LD = (BM * SCB / 4 + kThreads - 1) / kThreads;      // 4-byte loads per thread
-  static constexpr int SB_LD = (B_ROWS * SCB / 4 + kThreads - 1) / kThreads;
-  static constexpr int SA_N = BM * SCB / 4, SB_N = B_ROWS * SCB / 4;         // 4-byte words to load
-  static constexpr int LOADS = A_LD + B_LD + SA_LD + SB_LD;   // per thread per stage
+  static constexpr int A_N = BM * CB / 16, B_N = B_ROWS * CB / 16;          // 16-byte units
+  static constexpr int SA_N = BM * SCB / 4, SB_N = B_ROWS * SCB / 4;         // 4-byte units
+  static constexpr int A_LD = (A_N + NT - 1) / NT, B_LD = (B_N + NT - 1) / NT;
+  static constexpr int SA_LD = (SA_N + NT - 1) / NT, SB_LD = (SB_N + NT - 1) / NT;
+  static_assert(A_N % 64 == 0 && B_N % 64 == 0 && SA_N % 64 == 0 && SB_N % 64 == 0, "whole-wave loads");
 };
 
-template <int FMT, int BM, int BN, int CB, int MINB>
-__global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
-  using Lay = MxLayout<FMT, BM, BN, CB>;
+// NW wavefronts in a (NW / 2) x 2 grid over the tile; NS ring slots.
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS>
+__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
+  constexpr int NT = NW * 64;
+  using Lay = MxLayout<FMT, BM, BN, CB, NT>;
   constexpr int CPR = CB / 16;                    // 16-byte chunks per staged row
   constexpr int KS = CB / 64;                     // 128-element instruction steps per stage
+  constexpr int WM = NW / 2, RW = BM / WM;        // wavefront rows, rows per wavefront
   static_assert((BM == 128 || BM == 256) && (BN == 160 || BN == 224 || BN == 256) && (CB == 64 || CB == 128), "tile");
-  static_assert(Lay::SA_N % 64 == 0 && Lay::SB_N % 64 == 0, "whole-wave scale loads");
-  constexpr int FM = BM / 32, FN = BN / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * Lay::STAGE];
+  static_assert((NW == 4 || NW == 8) && (NS == 2 || NS == 3) && RW % 16 == 0, "layout");
+  constexpr int FM = RW / 16, FN = BN / 32;
+  // the ring, and after the K loop the epilogue's 16-row staging strips
+  constexpr int EPI = NW * 16 * (BN / 2 + 4) * 4;
+  constexpr int SMEM = NS * Lay::STAGE > EPI ? NS * Lay::STAGE : EPI;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -163,14 +186,14 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
   uint32_t offA[Lay::A_LD], offB[Lay::B_LD], offSA[Lay::SA_LD], offSB[Lay::SB_LD];
 #pragma unroll
   for (int i = 0; i < Lay::A_LD; ++i) {
-    const int s = i * kThreads + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
+    const int s = i * NT + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
     int64_t r = m0 + row;
     r = r < p.M ? r : p.M - 1;
     offA[i] = (uint32_t)(r * ldb + gch * 16);
   }
 #pragma unroll
   for (int i = 0; i < Lay::B_LD; ++i) {
-    const int s = i * kThreads + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
+    const int s = i * NT + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
     int64_t r = n0 + row;
     r = r < p.N ? r : p.N - 1;
     offB[i] = (uint32_t)(r * ldb + gch * 16);
@@ -179,14 +202,14 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
   constexpr int WPR = Lay::SCB / 4;               // words per row per stage
 #pragma unroll
   for (int i = 0; i < Lay::SA_LD; ++i) {
-    const int s = i * kThreads + tid;
+    const int s = i * NT + tid;
     int64_t r = m0 + s / WPR;
     r = r < p.M ? r : p.M - 1;
     offSA[i] = (uint32_t)(r * lds + (s % WPR) * 4);
   }
 #pragma unroll
   for (int i = 0; i < Lay::SB_LD; ++i) {
-    const int s = i * kThreads + tid;
+    const int s = i * NT + tid;
     int64_t r = n0 + s / WPR;
     r = r < p.N ? r : p.N - 1;
     offSB[i] = (uint32_t)(r * lds + (s % WPR) * 4);
@@ -197,18 +220,32 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
     const uint32_t st = smem_base + (uint32_t)((kt % NS) * Lay::STAGE);
     const uint32_t kc = (uint32_t)kt * CB, ksc = (uint32_t)kt * Lay::SCB;
 #pragma unroll
-    for (int i = 0; i < Lay::A_LD; ++i) dma16(p.A, offA[i] + kc, st + Lay::A_OFF + (i * kThreads + wave * 64) * 16);
+    for (int i = 0; i < Lay::A_LD; ++i)
+      if (i * NT + wave * 64 < Lay::A_N)                 // wave-uniform
+        dma16(p.A, offA[i] + kc, st + Lay::A_OFF + (i * NT + wave * 64) * 16);
 #pragma unroll
-    for (int i = 0; i < Lay::B_LD; ++i) dma16(p.B, offB[i] + kc, st + Lay::B_OFF + (i * kThreads + wave * 64) * 16);
+    for (int i = 0; i < Lay::B_LD; ++i)
+      if (i * NT + wave * 64 < Lay::B_N)
+        dma16(p.B, offB[i] + kc, st + Lay::B_OFF + (i * NT + wave * 64) * 16);
 #pragma unroll
     for (int i = 0; i < Lay::SA_LD; ++i)
-      if (i * kThreads + wave * 64 < Lay::SA_N)          // wave-uniform
-        dma4(p.As, offSA[i] + ksc, st + Lay::SA_OFF + (i * kThreads + wave * 64) * 4);
+      if (i * NT + wave * 64 < Lay::SA_N)
+        dma4(p.As, offSA[i] + ksc, st + Lay::SA_OFF + (i * NT + wave * 64) * 4);
 #pragma unroll
     for (int i = 0; i < Lay::SB_LD; ++i)
-      if (i * kThreads + wave * 64 < Lay::SB_N)
-        dma4(p.Bs, offSB[i] + ksc, st + Lay::SB_OFF + (i * kThreads + wave * 64) * 4);
+      if (i * NT + wave * 64 < Lay::SB_N)
+        dma4(p.Bs, offSB[i] + ksc, st + Lay::SB_OFF + (i * NT + wave * 64) * 4);
   };
+  // loads this wavefront issues per stage (wave-uniform)
+  int nload = 0;
+#pragma unroll
+  for (int i = 0; i < Lay::A_LD; ++i) nload += (i * NT + wave * 64 < Lay::A_N);
+#pragma unroll
+  for (int i = 0; i < Lay::B_LD; ++i) nload += (i * NT + wave * 64 < Lay::B_N);
+#pragma unroll
+  for (int i = 0; i < Lay::SA_LD; ++i) nload += (i * NT + wave * 64 < Lay::SA_N);
+#pragma unroll
+  for (int i = 0; i < Lay::SB_LD; ++i) nload += (i * NT + wave * 64 < Lay::SB_N);
 
   struct Frags {
     v8i a[FM], b[FN];
@@ -221,7 +258,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
     const int c = ks * 4 + g;                      // chunk within the staged row
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int row = wm * (BM / 2) + i * 16 + r16;
+      const int row = wm * RW + i * 16 + r16;
       const uint4 q = *reinterpret_cast<const uint4*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
       f.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
       f.sa[i] = st[Lay::SA_OFF + row * Lay::SCB + c];
@@ -250,17 +287,22 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
                                                                      0, f.sb[j]);
   };
 
-  // Stage kt lives in ring slot kt % 2.  At the top of iteration kt only
-  // the loads of stage kt are in flight; after the wait and the barrier
-  // they are visible to every wave and every wave has finished reading
-  // slot (kt + 1) % 2 (stage kt - 1), which then receives stage kt + 1.
-  // (A plain s_barrier, not __syncthreads: its release fence would also
-  // wait for loads that are meant to stay in flight.)
-  issue(0);
+  // Stage kt lives in ring slot kt % NS, and NS - 1 stages are loaded
+  // ahead.  At the top of iteration kt the wait leaves only the later
+  // stages' loads in flight; after the barrier stage kt is visible to every
+  // wave and every wave has finished reading stage kt - 1, whose slot then
+  // receives stage kt + NS - 1.  (A plain s_barrier, not __syncthreads: its
+  // release fence would also wait for loads that are meant to stay in
+  // flight.)
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < KT) issue(k);
   for (int kt = 0; kt < KT; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const int ahead = min(KT - 1 - kt, NS - 2);
+    wait_vm(ahead * nload);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (kt + 1 < KT) issue(kt + 1);
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
     if constexpr (FMT == FMT_MX) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -279,12 +321,14 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
         const int c = ks * 4 + g;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+#if FP4Q_NV_SCHED_SPLIT
           if (ks | h) __builtin_amdgcn_sched_barrier(0);
+#endif
           uint2 qa[FM], qb[FN];
           v2h sa[FM], sb[FN];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            const int row = wm * (BM / 2) + i * 16 + r16;
+            const int row = wm * RW + i * 16 + r16;
             qa[i] = *reinterpret_cast<const uint2*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4) + 8 * h);
             sa[i] = e4m3_to_h2(st[Lay::SA_OFF + row * Lay::SCB + 2 * c + h]);
           }
@@ -333,7 +377,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
         if constexpr (FMT == FMT_NV) v = v * tsc;
         stage[(g * 4 + r) * LDE + j * 16 + r16] = v;
       }
-    const int64_t row0 = m0 + wm * (BM / 2) + i * 16;
+    const int64_t row0 = m0 + wm * RW + i * 16;
 #pragma unroll
     for (int k = 0; k < (16 * WC / 4 + 63) / 64; ++k) {
       const int idx = k * 64 + lane;
@@ -362,20 +406,29 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_mx3(const MxArgs p) {
 #define FP4Q_MX_CB 128        // code bytes per row per stage
 #define FP4Q_MX_MINB 1        // workgroups per CU the register budget targets
 #endif
+#ifndef FP4Q_MX_NW
+#define FP4Q_MX_NW 8          // wavefronts per workgroup
+#define FP4Q_MX_NS 2          // LDS ring slots
+#endif
 #ifndef FP4Q_NV_BM
 #define FP4Q_NV_BM 256
 #define FP4Q_NV_BN 160
 #define FP4Q_NV_CB 64
 #endif
+#ifndef FP4Q_NV_NW
+#define FP4Q_NV_NW 8
+#define FP4Q_NV_NS 2
+#endif
 
 inline int cdiv_i(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <int FMT, int BM, int BN, int CB, int MINB>
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS>
 hipError_t launch_mx3(const MxArgs& a0, hipStream_t s) {
   MxArgs a = a0;
   a.tiles_m = cdiv_i(a.M, BM);
   a.tiles_n = cdiv_i(a.N, BN);
-  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB, NW, NS>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+                     dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -389,8 +442,9 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
   if (K % (2 * FP4Q_MX_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
     return launch_gemm_mxfp4_staged(a, as, b, bs, M, N, K, y, ldy, s);
   // 224 divides the common 7 * 2^k widths exactly; otherwise 256.
-  if (N % 224 == 0 && N % 256 != 0) return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB>(p, s);
-  return launch_mx3<FMT_MX, FP4Q_MX_BM, 256, FP4Q_MX_CB, FP4Q_MX_MINB>(p, s);
+  if (N % 224 == 0 && N % 256 != 0)
+    return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
+  return launch_mx3<FMT_MX, FP4Q_MX_BM, 256, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
 }
 
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
@@ -399,7 +453,7 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a
   if (K % (2 * FP4Q_NV_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
     return launch_gemm_nvfp4_staged(a, as, ats, b, bs, bts, M, N, K, y, ldy, s);
   MxArgs p{a, as, b, bs, ats, bts, M, N, K, y, ldy, 0, 0};
-  return launch_mx3<FMT_NV, FP4Q_NV_BM, FP4Q_NV_BN, FP4Q_NV_CB, 1>(p, s);
+  return launch_mx3<FMT_NV, FP4Q_NV_BM, FP4Q_NV_BN, FP4Q_NV_CB, 1, FP4Q_NV_NW, FP4Q_NV_NS>(p, s);
 }
 
 }  // namespace fp4q
