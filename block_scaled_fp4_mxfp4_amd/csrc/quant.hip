@@ -95,8 +95,14 @@ __device__ __forceinline__ int64_t chunk_offset(int64_t c, int64_t cpr, int64_t 
 // its partial max|x| to partial[blockIdx.x]; a one-workgroup finalize
 // kernel reduces the partials into the tensor-scale cell (amax encoding).
 // With direct != 0 (single workgroup) the cell is written at once.
-constexpr int kAmaxUnroll = 8;
-constexpr int kAmaxMaxGrid = 2048;
+#ifndef FP4Q_AMAX_UNROLL
+#define FP4Q_AMAX_UNROLL 2      // loads in flight per thread per iteration (measured best of 1..16)
+#endif
+constexpr int kAmaxUnroll = FP4Q_AMAX_UNROLL;
+#ifndef FP4Q_AMAX_GRID
+#define FP4Q_AMAX_GRID 512     // two workgroups per CU
+#endif
+constexpr int kAmaxMaxGrid = FP4Q_AMAX_GRID;
 
 template <bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t nchunks,
@@ -135,8 +141,17 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
 
 __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __restrict__ partial, int n,
                                                             uint32_t* __restrict__ cell) {
+  // every partial is loaded before any is used (n <= kAmaxMaxGrid = 2 x kThreads):
+  // one memory latency, not one per element
+  uint32_t q[kAmaxMaxGrid / kThreads];
+#pragma unroll
+  for (int j = 0; j < kAmaxMaxGrid / kThreads; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    q[j] = i < n ? partial[i] : 0u;
+  }
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partial[i]);   // non-negative floats
+#pragma unroll
+  for (int j = 0; j < kAmaxMaxGrid / kThreads; ++j) m = max(m, q[j]);     // non-negative floats
   for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   __shared__ uint32_t red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -150,7 +165,10 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
 
 // -------------------------------------------------------------- NVFP4 ----
 
-constexpr int kNvUnroll = 4;
+#ifndef FP4Q_NV_UNROLL
+#define FP4Q_NV_UNROLL 2        // 8-element chunks per thread (measured best of 1, 2, 4, 8)
+#endif
+constexpr int kNvUnroll = FP4Q_NV_UNROLL;
 
 template <bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
