@@ -32,6 +32,9 @@
 
 #include "internal.h"
 
+#ifndef FP4Q_EPI_NT
+#define FP4Q_EPI_NT 0           // 1: non-temporal output stores (measured slightly slower)
+#endif
 #ifndef FP4Q_NV_SCHED_SPLIT
 #define FP4Q_NV_SCHED_SPLIT 0   // 1: one scheduling region per 16-element block half
 #endif
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   constexpr int CPR = CB / 16;                    // 16-byte chunks per staged row
   constexpr int KS = CB / 64;                     // 128-element instruction steps per stage
   constexpr int WM = NW / 2, RW = BM / WM;        // wavefront rows, rows per wavefront
-  static_assert((BM == 128 || BM == 256) && (BN == 160 || BN == 224 || BN == 256) && (CB == 64 || CB == 128), "tile");
+  static_assert((BM == 128 || BM == 256 || BM == 512) && (BN == 160 || BN == 224 || BN == 256 || BN == 320) && (CB == 64 || CB == 128), "tile");
   static_assert((NW == 4 || NW == 8) && (NS == 2 || NS == 3) && RW % 16 == 0, "layout");
   constexpr int FM = RW / 16, FN = BN / 32;
   // the ring, and after the K loop the epilogue's 16-row staging strips
@@ -388,7 +391,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
         if (row < p.M) {
           float* dst = p.Y + row * p.ldy + col;
           if (vec && col + 4 <= p.N) {
+#if FP4Q_EPI_NT
             __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(dst));
+#else
+            *reinterpret_cast<v4f*>(dst) = v;
+#endif
           } else {
             if (col + 0 < p.N) dst[0] = v[0];
             if (col + 1 < p.N) dst[1] = v[1];
@@ -441,7 +448,8 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
   // K % 256 == 128 or tensors past 4 GiB: the register-staged kernel.
   if (K % (2 * FP4Q_MX_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
     return launch_gemm_mxfp4_staged(a, as, b, bs, M, N, K, y, ldy, s);
-  // 224 divides the common 7 * 2^k widths exactly; otherwise 256.
+  // 224 divides the common 7 * 2^k widths exactly; otherwise 256 (a
+  // round-count model that preferred 224 for 2048 x 14336 measured slower)
   if (N % 224 == 0 && N % 256 != 0)
     return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
   return launch_mx3<FMT_MX, FP4Q_MX_BM, 256, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
