@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(const GemmArgs p) {
 #define FP4Q_NV_TILE 128, 256, 1
 #endif
 #ifndef FP4Q_W16_TILE
-#define FP4Q_W16_TILE 256, 128, 1
+#define FP4Q_W16_TILE 128, 64, 4     // small tiles: the looped core has N, K in {768, 3072} (measured)
 #endif
 
 namespace {
