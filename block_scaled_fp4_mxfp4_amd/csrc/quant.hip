@@ -250,7 +250,10 @@ __device__ __forceinline__ void apply_chan_scale(float z[8], const float* __rest
   z[4] = z[4] * b.x; z[5] = z[5] * b.y; z[6] = z[6] * b.z; z[7] = z[7] * b.w;
 }
 
-constexpr int kMxUnroll = 2;
+#ifndef FP4Q_MX_UNROLL
+#define FP4Q_MX_UNROLL 2
+#endif
+constexpr int kMxUnroll = FP4Q_MX_UNROLL;
 
 template <bool BF16, bool CONTIG, bool SCALE, bool HAD>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
