@@ -415,6 +415,9 @@ hipError_t launch_gemm_nvfp4_staged(const uint8_t* a, const uint8_t* as, const f
 hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
                              const float* bts, int64_t M, int64_t N, int64_t K, float* y,
                              int64_t ldy, hipStream_t s) {
+#ifndef FP4Q_W16_STAGED_ONLY
+  if (w4a16_direct_supported(lda, M, N, K)) return launch_gemm_w4a16_direct(a, lda, b, bs, bts, M, N, K, y, ldy, s);
+#endif
   GemmArgs p{reinterpret_cast<const uint8_t*>(a), nullptr, nullptr, b, bs, bts, M, N, K, lda, y, ldy, 0, 0};
   return launch_tiled<FMT_W16, FP4Q_W16_TILE>(p, s);
 }

@@ -48,7 +48,30 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-enum { FMT_MX = 0, FMT_NV = 1 };
+enum { FMT_MX = 0, FMT_NV = 1, FMT_W16 = 2 };   // W16: bf16 A, NVFP4 B
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// 8 NVFP4 codes -> 8 exact bf16 values code * s_b (at most 6 significant
+// bits): the codes convert exactly to fp32, the fp32 product is exact and
+// the upper halves are the bf16 values.  (gfx950 has no packed bf16
+// multiply; the convert's own scale operand applies only the exponent.)
+__device__ __forceinline__ v8bf dequant8_bf16(uint32_t w, float sb) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo, hi;
+    switch (i) {
+      case 0: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); lo = p[0]; hi = p[1]; break; }
+      case 1: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); lo = p[0]; hi = p[1]; break; }
+      case 2: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); lo = p[0]; hi = p[1]; break; }
+      default: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); lo = p[0]; hi = p[1]; break; }
+    }
+    lo = lo * sb;
+    hi = hi * sb;
+    o[i] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
+  return __builtin_bit_cast(v8bf, uint4{o[0], o[1], o[2], o[3]});
+}
 
 // E4M3 block scale (non-negative byte) -> the same value in fp16 (every
 // E4M3 value, subnormals included, is an fp16 normal), splatted to both
@@ -83,7 +106,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 struct MxArgs {
-  const uint8_t* A;
+  const uint8_t* A;             // codes (MX, NV) or bf16 elements (W16)
   const uint8_t* As;
   const uint8_t* B;
   const uint8_t* Bs;
@@ -93,6 +116,7 @@ struct MxArgs {
   float* Y;
   int64_t ldy;
   int tiles_m, tiles_n;
+  int64_t lda;                  // W16: row stride of A in elements
 };
 
 constexpr int GROUP_M = 8;
@@ -147,14 +171,16 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 template <int FMT, int BM, int BN, int CB, int NT>
 struct MxLayout {
   static constexpr int B_ROWS = BN;
+  static constexpr int A_ROWB = FMT == FMT_W16 ? 4 * CB : CB;   // A bytes per row per stage
   static constexpr int A_OFF = 0;
-  static constexpr int B_OFF = A_OFF + BM * CB;
+  static constexpr int B_OFF = A_OFF + BM * A_ROWB;
   static constexpr int SA_OFF = B_OFF + B_ROWS * CB;
   static constexpr int SCB = FMT == FMT_MX ? CB / 16 : CB / 8;  // scale bytes per row per stage
-  static constexpr int SB_OFF = SA_OFF + BM * SCB;
+  static constexpr int SA_ROWS = FMT == FMT_W16 ? 0 : BM;       // bf16 A has no scales
+  static constexpr int SB_OFF = SA_OFF + SA_ROWS * SCB;
   static constexpr int STAGE = SB_OFF + B_ROWS * SCB;
-  static constexpr int A_N = BM * CB / 16, B_N = B_ROWS * CB / 16;          // 16-byte units
-  static constexpr int SA_N = BM * SCB / 4, SB_N = B_ROWS * SCB / 4;         // 4-byte units
+  static constexpr int A_N = BM * A_ROWB / 16, B_N = B_ROWS * CB / 16;      // 16-byte units
+  static constexpr int SA_N = SA_ROWS * SCB / 4, SB_N = B_ROWS * SCB / 4;    // 4-byte units
   static constexpr int A_LD = (A_N + NT - 1) / NT, B_LD = (B_N + NT - 1) / NT;
   static constexpr int SA_LD = (SA_N + NT - 1) / NT, SB_LD = (SB_N + NT - 1) / NT;
   static_assert(A_N % 64 == 0 && B_N % 64 == 0 && SA_N % 64 == 0 && SB_N % 64 == 0, "whole-wave loads");
@@ -168,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   constexpr int CPR = CB / 16;                    // 16-byte chunks per staged row
   constexpr int KS = CB / 64;                     // 128-element instruction steps per stage
   constexpr int WM = NW / 2, RW = BM / WM;        // wavefront rows, rows per wavefront
-  static_assert((BM == 128 || BM == 256 || BM == 512) && (BN == 160 || BN == 224 || BN == 256 || BN == 320) && (CB == 64 || CB == 128), "tile");
+  static_assert(BM % 64 == 0 && BM <= 512 && BN % 32 == 0 && BN <= 320 && (CB == 64 || CB == 128), "tile");
   static_assert((NW == 4 || NW == 8) && (NS == 2 || NS == 3) && RW % 16 == 0, "layout");
   constexpr int FM = RW / 16, FN = BN / 32;
   // the ring, and after the K loop the epilogue's 16-row staging strips
@@ -186,13 +212,24 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 
   // ---- per-thread byte offsets of the direct loads (row and chunk are
   // fixed over K; the stage adds kt * 128 bytes of codes / 8 of scales).
-  uint32_t offA[Lay::A_LD], offB[Lay::B_LD], offSA[Lay::SA_LD], offSB[Lay::SB_LD];
+  uint32_t offA[Lay::A_LD], offB[Lay::B_LD], offSA[Lay::SA_LD > 0 ? Lay::SA_LD : 1], offSB[Lay::SB_LD];
 #pragma unroll
   for (int i = 0; i < Lay::A_LD; ++i) {
-    const int s = i * NT + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
-    int64_t r = m0 + row;
-    r = r < p.M ? r : p.M - 1;
-    offA[i] = (uint32_t)(r * ldb + gch * 16);
+    if constexpr (FMT == FMT_W16) {
+      // bf16 rows of 4 CB bytes per stage; 16-byte chunk c of row r is
+      // stored at position c ^ (r % 16), so the 16 rows a fragment read
+      // touches fall on 16 different positions
+      constexpr int CPA = Lay::A_ROWB / 16;
+      const int s = i * NT + tid, row = s / CPA, gch = (s % CPA) ^ (row & 15);
+      int64_t r = m0 + row;
+      r = r < p.M ? r : p.M - 1;
+      offA[i] = (uint32_t)(r * p.lda * 2 + gch * 16);
+    } else {
+      const int s = i * NT + tid, row = s / CPR, gch = (s % CPR) ^ swz<CB>(row);
+      int64_t r = m0 + row;
+      r = r < p.M ? r : p.M - 1;
+      offA[i] = (uint32_t)(r * ldb + gch * 16);
+    }
   }
 #pragma unroll
   for (int i = 0; i < Lay::B_LD; ++i) {
@@ -221,11 +258,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   const uint32_t smem_base = lds_offset(smem);
   auto issue = [&](int kt) {
     const uint32_t st = smem_base + (uint32_t)((kt % NS) * Lay::STAGE);
-    const uint32_t kc = (uint32_t)kt * CB, ksc = (uint32_t)kt * Lay::SCB;
+    const uint32_t kc = (uint32_t)kt * CB, ksc = (uint32_t)kt * Lay::SCB, kca = (uint32_t)kt * Lay::A_ROWB;
 #pragma unroll
     for (int i = 0; i < Lay::A_LD; ++i)
       if (i * NT + wave * 64 < Lay::A_N)                 // wave-uniform
-        dma16(p.A, offA[i] + kc, st + Lay::A_OFF + (i * NT + wave * 64) * 16);
+        dma16(p.A, offA[i] + kca, st + Lay::A_OFF + (i * NT + wave * 64) * 16);
 #pragma unroll
     for (int i = 0; i < Lay::B_LD; ++i)
       if (i * NT + wave * 64 < Lay::B_N)
@@ -314,6 +351,44 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
         load_frags(f, kt, ks);
         mma(f);
       }
+    } else if constexpr (FMT == FMT_W16) {
+      // bf16 A x NVFP4 B: the same K assignment as the NVFP4 path (lane
+      // group g, block half h, slice s2 -> elements 32 c + 16 h + 8 s2 of
+      // chunk c), A read as 16-byte bf16 chunks, B dequantized exactly to
+      // bf16, bf16 matrix core
+      const uint8_t* st = smem + (kt % NS) * Lay::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks * 4 + g;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint2 qb[FN];
+          float sbf[FN];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int row = wn * (BN / 2) + j * 16 + r16;
+            qb[j] = *reinterpret_cast<const uint2*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4) + 8 * h);
+            sbf[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st[Lay::SB_OFF + row * Lay::SCB + 2 * c + h], 1.0f, false)[0];
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            v8bf ha[FM];
+            const int ch = 16 * ks + 4 * g + 2 * h + s2;     // bf16 chunk within the staged row
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              const int row = wm * RW + i * 16 + r16;
+              ha[i] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF + row * Lay::A_ROWB + ((ch ^ (row & 15)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const v8bf hb = dequant8_bf16(s2 ? qb[j].y : qb[j].x, sbf[j]);
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[i], hb, acc[i][j], 0, 0, 0);
+            }
+          }
+        }
+      }
     } else {
       // NVFP4: lane group g owns elements [32 c, 32 c + 32) of chunk c; each
       // half h is one 16-element block, consumed as two 8-element slices by
@@ -369,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   float* stage = reinterpret_cast<float*>(smem) + wave * 16 * LDE;
   const int64_t col0 = n0 + wn * WC;
   const bool vec = ((p.ldy & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.Y) & 15) == 0);
-  const float tsc = FMT == FMT_NV ? (*p.Ats) * (*p.Bts) : 1.0f;
+  const float tsc = FMT == FMT_NV ? (*p.Ats) * (*p.Bts) : FMT == FMT_W16 ? *p.Bts : 1.0f;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -377,7 +452,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = acc[i][j][r];
-        if constexpr (FMT == FMT_NV) v = v * tsc;
+        if constexpr (FMT != FMT_MX) v = v * tsc;
         stage[(g * 4 + r) * LDE + j * 16 + r16] = v;
       }
     const int64_t row0 = m0 + wm * RW + i * 16;
@@ -453,6 +528,25 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
   if (N % 224 == 0 && N % 256 != 0)
     return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
   return launch_mx3<FMT_MX, FP4Q_MX_BM, 256, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
+}
+
+#ifndef FP4Q_W16M_BM
+#define FP4Q_W16M_BM 128      // small tiles: the looped core has N, K in {768, 3072} (measured)
+#define FP4Q_W16M_BN 64
+#define FP4Q_W16M_CB 64
+#define FP4Q_W16M_NW 8
+#endif
+
+bool w4a16_direct_supported(int64_t lda, int64_t M, int64_t N, int64_t K) {
+  return K % (2 * FP4Q_W16M_CB) == 0 && lda % 8 == 0 && M * lda * 2 < (int64_t(1) << 32) &&
+         N * (K / 2) < (int64_t(1) << 32);
+}
+
+hipError_t launch_gemm_w4a16_direct(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
+                                    const float* bts, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
+                                    hipStream_t s) {
+  MxArgs p{reinterpret_cast<const uint8_t*>(a), nullptr, b, bs, nullptr, bts, M, N, K, y, ldy, 0, 0, lda};
+  return launch_mx3<FMT_W16, FP4Q_W16M_BM, FP4Q_W16M_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2>(p, s);
 }
 
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,

@@ -43,6 +43,11 @@ hipError_t launch_gemm_nvfp4_staged(const uint8_t* a, const uint8_t* as, const f
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,
                              const uint8_t* b, const uint8_t* bs, const float* bts, int64_t M,
                              int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s);
+// W4A16 on the direct-load pipeline (gemm_mx.hip), when the shape allows it
+bool w4a16_direct_supported(int64_t lda, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_w4a16_direct(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
+                                    const float* bts, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
+                                    hipStream_t s);
 hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
                              const float* bts, int64_t M, int64_t N, int64_t K, float* y,
                              int64_t ldy, hipStream_t s);
