@@ -88,6 +88,14 @@ __device__ __forceinline__ int64_t chunk_offset(int64_t c, int64_t cpr, int64_t 
   return r * ld + (c - r * cpr) * 8;
 }
 
+// Chunk actually loaded for index c: past the end, the last chunk.  Loads
+// stay unconditional -- a load under a branch makes the compiler wait for it
+// before the next one is issued -- and what a clamped load brings in is
+// never stored (nor can it change a maximum).
+__device__ __forceinline__ int64_t clamp_chunk(int64_t c, int64_t n) { return c < n ? c : n - 1; }
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------- amax ----
 
 // Tensor maximum in two steps without atomics (many workgroups updating
@@ -96,7 +104,7 @@ __device__ __forceinline__ int64_t chunk_offset(int64_t c, int64_t cpr, int64_t 
 // kernel reduces the partials into the tensor-scale cell (amax encoding).
 // With direct != 0 (single workgroup) the cell is written at once.
 #ifndef FP4Q_AMAX_UNROLL
-#define FP4Q_AMAX_UNROLL 2      // loads in flight per thread per iteration (measured best of 1..16)
+#define FP4Q_AMAX_UNROLL 8      // loads in flight per thread per iteration (measured best of 2, 4, 8)
 #endif
 constexpr int kAmaxUnroll = FP4Q_AMAX_UNROLL;
 #ifndef FP4Q_AMAX_GRID
@@ -108,34 +116,43 @@ template <bool BF16, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t nchunks,
                                                    int64_t cpr, int64_t ld,
                                                    uint32_t* __restrict__ out, int direct) {
-  float m = 0.0f;
+  // max|x| on the bit patterns: non-negative floats order like unsigned ints
+  constexpr int W = BF16 ? 4 : 8;             // dwords per 8-element chunk
+  uint32_t m = 0;
+  us2 m2 = {0, 0};
   const int64_t stride = (int64_t)gridDim.x * kThreads * kAmaxUnroll;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * kAmaxUnroll + threadIdx.x; c0 < nchunks; c0 += stride) {
-    float v[kAmaxUnroll][8];
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kAmaxUnroll; base < nchunks; base += stride) {
+    uint32_t raw[kAmaxUnroll][W];
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {           // all loads first
-      const int64_t c = c0 + (int64_t)u * kThreads;
-      if (c < nchunks) {
-        load8<BF16>(x, chunk_offset<CONTIG>(c, cpr, ld), v[u]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+      const int64_t c = clamp_chunk(base + u * kThreads + threadIdx.x, nchunks);
+      const uint4* p = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const char*>(x) + chunk_offset<CONTIG>(c, cpr, ld) * (BF16 ? 2 : 4));
+      const uint4 q = p[0];
+      raw[u][0] = q.x; raw[u][1] = q.y; raw[u][2] = q.z; raw[u][3] = q.w;
+      if constexpr (!BF16) {
+        const uint4 q2 = p[1];
+        raw[u][4] = q2.x; raw[u][5] = q2.y; raw[u][6] = q2.z; raw[u][7] = q2.w;
       }
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[u][i]));
+      for (int i = 0; i < W; ++i) {
+        if constexpr (BF16) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, raw[u][i] & 0x7FFF7FFFu));
+        else m = max(m, raw[u][i] & 0x7FFFFFFFu);
+      }
   }
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  __shared__ float red[kThreads / 64];
+  if constexpr (BF16) m = (uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16;
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  __shared__ uint32_t red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
 #pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, red[i]);
-    if (direct) out[0] = kAmaxFlag | __float_as_uint(m);
-    else out[blockIdx.x] = __float_as_uint(m);
+    for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+    if (direct) out[0] = kAmaxFlag | m;
+    else out[blockIdx.x] = m;
   }
 }
 
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
 #pragma unroll
   for (int j = 0; j < kAmaxMaxGrid / kThreads; ++j) {
     const int i = threadIdx.x + j * kThreads;
-    q[j] = i < n ? partial[i] : 0u;
+    q[j] = partial[i < n ? i : n - 1];
   }
   uint32_t m = 0;
 #pragma unroll
@@ -181,12 +198,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 #pragma unroll
   for (int u = 0; u < kNvUnroll; ++u) {
     cidx[u] = ((int64_t)blockIdx.x * kNvUnroll + u) * kThreads + threadIdx.x;
-    if (cidx[u] < nchunks) {
-      load8<BF16>(x, chunk_offset<CONTIG>(cidx[u], cpr, ld), v[u]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
-    }
+    load8<BF16>(x, chunk_offset<CONTIG>(clamp_chunk(cidx[u], nchunks), cpr, ld), v[u]);
   }
 #pragma unroll
   for (int u = 0; u < kNvUnroll; ++u) {
@@ -259,24 +271,21 @@ template <bool BF16, bool CONTIG, bool SCALE, bool HAD>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
     const float* __restrict__ t, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  float v[kMxUnroll][8];
+  float v[kMxUnroll][8], ts[SCALE ? kMxUnroll : 1][8];
   int64_t cidx[kMxUnroll];
 #pragma unroll
-  for (int u = 0; u < kMxUnroll; ++u) {
+  for (int u = 0; u < kMxUnroll; ++u) {              // all loads first
     cidx[u] = ((int64_t)blockIdx.x * kMxUnroll + u) * kThreads + threadIdx.x;
-    if (cidx[u] < nchunks) {
-      load8<BF16>(x, chunk_offset<CONTIG>(cidx[u], cpr, ld), v[u]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
-    }
+    const int64_t cl = clamp_chunk(cidx[u], nchunks);
+    load8<BF16>(x, chunk_offset<CONTIG>(cl, cpr, ld), v[u]);
+    if constexpr (SCALE) load8<false>(t, (cl % cpr) * 8, ts[u]);
   }
   const int qlane = threadIdx.x & 3;
 #pragma unroll
   for (int u = 0; u < kMxUnroll; ++u) {
     if constexpr (SCALE) {
-      const int64_t c = cidx[u] < nchunks ? cidx[u] : 0;
-      apply_chan_scale(v[u], t, (c % cpr) * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] * ts[u][i];
     }
     if constexpr (HAD) hadamard32_lane(v[u], qlane);
     float a = 0.0f;
@@ -300,14 +309,10 @@ __global__ __launch_bounds__(kThreads) void k_hadamard32(
     const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
     const float* __restrict__ t, float* __restrict__ y, int64_t ldy) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t cl = clamp_chunk(c, nchunks);
   float v[8];
-  if (c < nchunks) {
-    load8<BF16>(x, chunk_offset<CONTIG>(c, cpr, ld), v);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  if constexpr (SCALE) apply_chan_scale(v, t, ((c < nchunks ? c : 0) % cpr) * 8);
+  load8<BF16>(x, chunk_offset<CONTIG>(cl, cpr, ld), v);
+  if constexpr (SCALE) apply_chan_scale(v, t, (cl % cpr) * 8);
   hadamard32_lane(v, threadIdx.x & 3);
   if (c < nchunks) {
     const int64_t r = c / cpr;
@@ -392,7 +397,10 @@ struct SdArgs {
   int32_t nseg;
 };
 
-constexpr int kSdUnroll = 2;
+#ifndef FP4Q_SD_UNROLL
+#define FP4Q_SD_UNROLL 2        // chunks per thread
+#endif
+constexpr int kSdUnroll = FP4Q_SD_UNROLL;
 
 __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int steps,
                                                           int64_t bank_stride) {
@@ -405,15 +413,19 @@ __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int
   float* __restrict__ res = args.res[seg];
   float x[kSdUnroll][8], r[kSdUnroll][8];
   int64_t cidx[kSdUnroll];
+  uint32_t sb_raw[kSdUnroll];
+#pragma unroll
+  for (int u = 0; u < kSdUnroll; ++u) {              // all loads first
+    cidx[u] = (wg * kSdUnroll + u) * kThreads + threadIdx.x;
+    const int64_t cl = clamp_chunk(cidx[u], n);
+    load8<false>(w, cl * 8, x[u]);
+    load8<false>(res, cl * 8, r[u]);
+    sb_raw[u] = args.scales[seg][cl >> 1];
+  }
 #pragma unroll
   for (int u = 0; u < kSdUnroll; ++u) {
-    cidx[u] = (wg * kSdUnroll + u) * kThreads + threadIdx.x;
     const bool in = cidx[u] < n;
-    if (in) {
-      load8<false>(w, cidx[u] * 8, x[u]);
-      load8<false>(res, cidx[u] * 8, r[u]);
-    }
-    const uint32_t sb = in ? args.scales[seg][cidx[u] >> 1] : 0u;
+    const uint32_t sb = in ? sb_raw[u] : 0u;
     const float s = st * e4m3_decode(sb);
     const float rho = 1.0f / s;
 #pragma unroll

@@ -90,6 +90,88 @@ def test_nvfp4_prefill_full_size_sampled_rows():
         _nv_check(xf, dev_bf16(b), rows=sample_rows(b.shape[0], seed=hash(name) % 1000))
 
 
+def test_nvfp4_dynamic_large_tensor():
+    # 8192 x 7168 bf16 (58.7 M elements): the amax pass runs at its largest
+    # grid, and the partial maxima fill the front of the block-scale buffer
+    b = synth.f32_to_bf16_bits(synth.heavy_tailed_f32(105, 106, (8192, 7168)))
+    xf = OF.bf16_bits_to_f32(b)
+    _nv_check(xf, dev_bf16(b), rows=sample_rows(b.shape[0], seed=7))
+
+
+def _nv_ref(x_f32_host):
+    """Oracle codes, scales and tensor scale as device tensors."""
+    st = ONV.tensor_scale_from_amax(np.abs(x_f32_host).max())
+    c, sc, _ = ONV.quantize(x_f32_host, tensor_scale=st)
+    return (torch.from_numpy(packed(c)).to("cuda:0"), torch.from_numpy(np.ascontiguousarray(sc)).to("cuda:0"),
+            torch.tensor([st], dtype=torch.float32, device="cuda:0"))
+
+
+def _same(got, want):
+    return all(torch.equal(g, w) for g, w in zip(got, want))
+
+
+def test_nvfp4_dynamic_repeated_calls_streams_and_graph():
+    """Dynamic quantization many times in a row, from two side streams
+    without host synchronisation, and replayed from a captured graph with
+    the input changed between replays (the amax, finalize and quantize
+    launches all go into the graph): every result must equal the oracle's."""
+    L = fp4q()
+    ba = synth.f32_to_bf16_bits(synth.heavy_tailed_f32(111, 112, (48, 160)))        # one workgroup
+    bb = synth.f32_to_bf16_bits(synth.heavy_tailed_f32(113, 114, (1000, 4096)))     # ~250 workgroups
+    bb2 = synth.f32_to_bf16_bits(synth.normal_f32(115, (1000, 4096), sigma=0.3))    # same shape, other max
+    xc = synth.heavy_tailed_f32(116, 117, (300, 1040))                              # fp32, strided view
+    xa_d, xb_d, xb2_d = dev_bf16(ba), dev_bf16(bb), dev_bf16(bb2)
+    xc_full = dev_f32(xc)
+    xc_d = xc_full[:, :1024]
+    ref = {"a": _nv_ref(OF.bf16_bits_to_f32(ba)), "b": _nv_ref(OF.bf16_bits_to_f32(bb)),
+           "b2": _nv_ref(OF.bf16_bits_to_f32(bb2)), "c": _nv_ref(np.ascontiguousarray(xc[:, :1024]))}
+    inputs = {"a": xa_d, "b": xb_d, "b2": xb2_d, "c": xc_d}
+
+    # 1: one stream, 70 calls
+    order = ["a", "b", "c", "b2"] * 18
+    outs = [(k, L.quantize_nvfp4(inputs[k])) for k in order[:70]]
+    torch.cuda.synchronize()
+    for i, (k, o) in enumerate(outs):
+        assert _same(o, ref[k]), f"call {i} ({k})"
+
+    # 2: two side streams, launches interleaved, no host synchronisation
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(12):
+        with torch.cuda.stream(s1):
+            outs.append(("b", L.quantize_nvfp4(xb_d)))
+        with torch.cuda.stream(s2):
+            k = "a" if i % 2 else "c"
+            outs.append((k, L.quantize_nvfp4(inputs[k])))
+    torch.cuda.synchronize()
+    for i, (k, o) in enumerate(outs):
+        assert _same(o, ref[k]), f"side-stream call {i} ({k})"
+
+    # 3: graph replays; the static input alternates between two tensors
+    # whose maxima differ, with eager library calls between the replays
+    static_in = xb_d.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.quantize_nvfp4(static_in)              # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gout = L.quantize_nvfp4(static_in)
+    for i in range(6):
+        k = "b2" if i % 2 else "b"
+        static_in.copy_(inputs[k])
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(gout, ref[k]), f"replay {i} ({k})"
+        eager = L.quantize_nvfp4(xa_d)
+        torch.cuda.synchronize()
+        assert _same(eager, ref["a"]), f"eager call after replay {i}"
+
+
 def test_mxfp4_e2m1_rounding_sweep():
     # blocks whose maximum is 7.5 get e = 0, so the element values themselves
     # are rounded; sweep every float32 near each decision and grid point
