@@ -377,6 +377,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
               const int row = wm * RW + i * 16 + r16;
               ha[i] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF + row * Lay::A_ROWB + ((ch ^ (row & 15)) << 4));
             }
+            __builtin_amdgcn_s_setprio(1);      // as in the NVFP4 path
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
               const v8bf hb = dequant8_bf16(s2 ? qb[j].y : qb[j].x, sbf[j]);
@@ -384,6 +385,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
               for (int i = 0; i < FM; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[i], hb, acc[i][j], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
           }
         }
       }
@@ -400,14 +402,16 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 #if FP4Q_NV_SCHED_SPLIT
           if (ks | h) __builtin_amdgcn_sched_barrier(0);
 #endif
-          uint2 qa[FM], qb[FN];
-          v2h sa[FM], sb[FN];
+          uint2 qa[FM];
+          v2h sa[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const int row = wm * RW + i * 16 + r16;
             qa[i] = *reinterpret_cast<const uint2*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4) + 8 * h);
             sa[i] = e4m3_to_h2(st[Lay::SA_OFF + row * Lay::SCB + 2 * c + h]);
           }
+          uint2 qb[FN];
+          v2h sb[FN];
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int row = wn * (BN / 2) + j * 16 + r16;
@@ -419,6 +423,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
             v8h ha[FM];
 #pragma unroll
             for (int i = 0; i < FM; ++i) ha[i] = dequant8(s2 ? qa[i].y : qa[i].x, sa[i]);
+            // raised wave priority for the matrix instructions: the wavefront
+            // in its multiply block goes first, so the two wavefronts of a
+            // SIMD drift apart and one's dequantization overlaps the other's
+            // multiplies (measured +1%)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
               const v8h hb = dequant8(s2 ? qb[j].y : qb[j].x, sb[j]);
@@ -426,6 +435,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
               for (int i = 0; i < FM; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i], hb, acc[i][j], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
           }
         }
       }
