@@ -83,6 +83,23 @@ def test_mxfp4_gemm_small_ragged(M, N, K):
     _check(y, OG.w4a4_mxfp4(cx, sx, cw, sw), f"mxfp4 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 8192, 256), (200, 300, 512)])
+def test_mxfp4_gemm_both_column_tiles(M, N, K):
+    # the launcher picks the column tile by rounds over the compute units:
+    # 2048 x 8192 fills one round with 256-wide tiles (224 would need two);
+    # 200 x 300 takes 224-wide tiles, ragged in both M and N
+    x = synth.heavy_tailed_f32(220 + M, 221, (M, K))
+    w = synth.normal_f32(222 + N, (N, K), 0.02)
+    L = fp4q()
+    ac, as_ = L.quantize_mxfp4(dev_f32(x), None, True)
+    bc, bs = L.quantize_mxfp4(dev_f32(w), None, True)
+    y = host(L.gemm_w4a4(L.MXFP4, ac, as_, None, bc, bs, None))
+    rows, cols = sample_rows(M, 40, 5), sample_rows(N, 200, 6)
+    cx, sx = OMX.quantize(OMX.hadamard32_scale(x[rows]))
+    cw, sw = OMX.quantize(OMX.hadamard32_scale(w[cols]))
+    _check(y[np.ix_(rows, cols)], OG.w4a4_mxfp4(cx, sx, cw, sw), f"mxfp4 {M}x{N}x{K}")
+
+
 def test_mxfp4_transform_full_size_sampled():
     wl = synth.mxfp4_transform()
     xb, wb = wl.arrays["x_bf16"], wl.arrays["w_bf16"]
