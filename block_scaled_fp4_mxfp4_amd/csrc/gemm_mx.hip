@@ -582,8 +582,14 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
 
 #ifndef FP4Q_W16M_BM
 #define FP4Q_W16M_BM 128      // small tiles: the looped core has N, K in {768, 3072} (measured)
-#define FP4Q_W16M_BN 64
+#endif
+#ifndef FP4Q_W16M_BN
+#define FP4Q_W16M_BN 96       // 768-wide outputs: 8 x 32 = 256 tiles at M = 4096 (measured best of 64, 96, 128)
+#endif
+#ifndef FP4Q_W16M_CB
 #define FP4Q_W16M_CB 64
+#endif
+#ifndef FP4Q_W16M_NW
 #define FP4Q_W16M_NW 8
 #endif
 
