@@ -797,15 +797,7 @@ hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8
   if (M > FP4Q_DEC_ROWS_MAXM && stream_supported(N, K)) {
     const StLayout L = st_layout((int)K);
     // spread the rows evenly over one workgroup per compute unit
-    static int n_cu = 0;
-    if (!n_cu) {
-      int dev = 0, v = 0;
-      if (hipGetDevice(&dev) == hipSuccess &&
-          hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-        n_cu = v;
-      else
-        n_cu = 256;
-    }
+    const int n_cu = device_cus();
     const int64_t groups = (N + 15) / 16;
     int64_t grid = groups < n_cu ? groups : n_cu;
     const int64_t rpw = (N + grid - 1) / grid;

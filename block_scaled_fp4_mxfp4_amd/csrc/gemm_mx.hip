@@ -529,8 +529,19 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 
 inline int cdiv_i(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Compute units of the current device (cached per device; 256 if the query
-// fails).
+
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS>
+hipError_t launch_mx3(const MxArgs& a0, hipStream_t s) {
+  MxArgs a = a0;
+  a.tiles_m = cdiv_i(a.M, BM);
+  a.tiles_n = cdiv_i(a.N, BN);
+  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB, NW, NS>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+                     dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 int device_cus() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -545,18 +556,6 @@ int device_cus() {
   }
   return v;
 }
-
-template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS>
-hipError_t launch_mx3(const MxArgs& a0, hipStream_t s) {
-  MxArgs a = a0;
-  a.tiles_m = cdiv_i(a.M, BM);
-  a.tiles_n = cdiv_i(a.N, BN);
-  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB, NW, NS>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
-                     dim3(NW * 64), 0, s, a);
-  return hipGetLastError();
-}
-
-}  // namespace
 
 hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,

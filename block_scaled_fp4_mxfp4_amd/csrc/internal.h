@@ -10,6 +10,10 @@
 
 namespace fp4q {
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int device_cus();
+
 hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
                               hipStream_t s);
