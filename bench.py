@@ -52,8 +52,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the per-GPU kernels are the whole "
-              "hot path and multi-GPU sharding is described in the design notes, not built.",
+        print("bench.py: runs on one GPU only (--gpus 1); the kernels measured here are the whole "
+              "per-GPU hot path, and splitting the layer over several GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 
