@@ -72,6 +72,17 @@ def test_validation_happens_before_any_device_work(fp4q):
     arr2 = (fp4q.SdSegment * 1)(seg2)
     assert L.fp4q_sigma_delta_requant(arr2, 1, 4, 32, None) == 5                             # bank stride < 64
     assert L.fp4q_balance_scale(fake16, 0, 4, 4, 4, fake16, 0, 4, 4, 1.5, fake16, fake16, None) == 5
+    # empty tensors are refused (BAD_SHAPE), never launched
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 0, 32, 32, fake16, fake, fake, 0, None) == 2
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 0, 0, fake16, fake, fake, 0, None) == 2
+    assert L.fp4q_quantize_mxfp4(fake16, 1, 0, 64, 64, None, 1, fake16, fake, None) == 2
+    assert L.fp4q_hadamard32_scale(fake16, 1, 0, 64, 64, None, fake16, 64, None) == 2
+    for m, n, k in ((0, 4, 128), (4, 0, 128), (4, 4, 0)):
+        assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, m, n, k, fake16, 4, None) == 2
+        assert L.fp4q_gemm_w4a16(fake16, 128, fake16, fake16, fake, m, n, k, fake16, 4, None) == 2
+        assert L.fp4q_linear_w4a4(fake16, 128, fake, 0, fake16, fake16, fake, m, n, k, fake16, 8, None) == 2
+    seg0 = fp4q.SdSegment(0x10000, 0x1000, 0x1000, 0x10000, 0x10000, 0, 32)
+    assert L.fp4q_sigma_delta_requant((fp4q.SdSegment * 1)(seg0), 1, 1, 0, None) == 2
 
 
 def test_device_check_without_gpu(fp4q):
