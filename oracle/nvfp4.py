@@ -15,6 +15,9 @@ Definition followed:
   and W4A4": the block scale is the block maximum / 6 (before the tensor
   scale is divided out); block max/RMS is at most 4 in a 16-element block.
 
+* loopquant page, section 2.2 and the section 2.5 listing: the 4/6 block
+  scaling (``rule="4/6"`` of :func:`quantize`).
+
 The order of the fp32 operations is the reading this project takes where the
 pages are silent (recorded in the design notes): every step is a single
 IEEE binary32 operation with round-to-nearest-even.
@@ -57,22 +60,12 @@ def block_scales(x: np.ndarray, s_t) -> np.ndarray:
     return e4m3_ceil(y.astype(np.float64))
 
 
-def quantize(x: np.ndarray, tensor_scale=None):
-    """NVFP4-quantize a float32 [R, K] tensor.
-
-    Returns ``(codes, scales, s_t)``: ``codes`` uint8 [R, K] (one 4-bit code
-    per element, unpacked), ``scales`` uint8 [R, K/16] (E4M3 bytes),
-    ``s_t`` float32.  With ``tensor_scale`` given it is used as s_t.
-    """
-    x = np.asarray(x, dtype=F32)
+def _encode_with(x: np.ndarray, s_t, sb_bytes: np.ndarray):
+    """Codes of ``x`` under the given block-scale bytes, and the decoded
+    total scales s = fl(s_t * s_b) per block."""
     R, K = x.shape
-    if tensor_scale is None:
-        s_t = tensor_scale_from_amax(np.abs(x).max() if x.size else F32(0))
-    else:
-        s_t = F32(tensor_scale)
-    sb_bytes = block_scales(x, s_t)
     s_b = e4m3_decode(sb_bytes).astype(F32)                      # exact in fp32
-    s = (s_t * s_b).astype(F32)                                  # fl32 product
+    s = (F32(s_t) * s_b).astype(F32)                             # fl32 product
     with np.errstate(divide="ignore"):
         rho = (F32(1.0) / s).astype(F32)                         # fl32 reciprocal
     rho_e = np.repeat(rho, BLOCK, axis=1)
@@ -83,7 +76,72 @@ def quantize(x: np.ndarray, tensor_scale=None):
         codes[r0:r0 + 256] = e2m1_round(v[r0:r0 + 256])
     zero_blk = np.repeat(s == 0, BLOCK, axis=1)
     codes[zero_blk] = 0
-    return codes, sb_bytes, s_t
+    return codes, s
+
+
+def block_scales_to(x: np.ndarray, s_t, target) -> np.ndarray:
+    """E4M3 block-scale bytes that map each block maximum to ``target`` (6
+    or 4): ceil_E4M3(fl(a_b / fl(target * s_t)))."""
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    s_t = F32(s_t)
+    a_b = np.abs(x).reshape(R, K // BLOCK, BLOCK).max(axis=-1)       # exact
+    t_st = F32(F32(target) * s_t)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        y = (a_b / t_st).astype(F32)                                  # fl32 division
+    y = np.where((a_b == 0) | (s_t == 0), F32(0), y)
+    return e4m3_ceil(y.astype(np.float64))
+
+
+def block_sq_error(x: np.ndarray, codes: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Squared reconstruction error of every 16-block, in binary32, in this
+    fixed order (the reading taken for the 4/6 choice; the pages give none):
+        d_i = fl(x_i - fl(s * value(code_i))),  e_i = fl(d_i * d_i)
+        T(h) = ((e0 + e1) + (e2 + e3)) + ((e4 + e5) + (e6 + e7))  per 8-element half
+        E = fl(T(first half) + T(second half))"""
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    q = e2m1_decode(codes).astype(F32)                           # exact
+    se = np.repeat(np.asarray(s, dtype=F32), BLOCK, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        d = (x - (se * q).astype(F32)).astype(F32)
+        e = (d * d).astype(F32).reshape(R, K // BLOCK, 2, 8)
+        p1 = (e[..., 0::2] + e[..., 1::2]).astype(F32)
+        p2 = (p1[..., 0::2] + p1[..., 1::2]).astype(F32)
+        t = (p2[..., 0] + p2[..., 1]).astype(F32)
+        return (t[..., 0] + t[..., 1]).astype(F32)
+
+
+def quantize(x: np.ndarray, tensor_scale=None, rule: str = "6"):
+    """NVFP4-quantize a float32 [R, K] tensor.
+
+    Returns ``(codes, scales, s_t)``: ``codes`` uint8 [R, K] (one 4-bit code
+    per element, unpacked), ``scales`` uint8 [R, K/16] (E4M3 bytes),
+    ``s_t`` float32.  With ``tensor_scale`` given it is used as s_t.
+
+    ``rule="6"`` maps every block maximum to 6.  ``rule="4/6"`` is the 4/6
+    block scaling of the loopquant page (section 2.2, residue-bound paragraph;
+    ``block_scale_46`` in the section 2.5 listing): both candidate scales,
+    block maximum to 6 and to 4, keep |x / s| <= 6, and each block takes the
+    one with the smaller squared error (:func:`block_sq_error`); ties go to 6.
+    """
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    if tensor_scale is None:
+        s_t = tensor_scale_from_amax(np.abs(x).max() if x.size else F32(0))
+    else:
+        s_t = F32(tensor_scale)
+    sb6 = block_scales(x, s_t)
+    codes6, s6 = _encode_with(x, s_t, sb6)
+    if rule == "6":
+        return codes6, sb6, s_t
+    assert rule == "4/6", rule
+    sb4 = block_scales_to(x, s_t, 4)
+    codes4, s4 = _encode_with(x, s_t, sb4)
+    pick4 = block_sq_error(x, codes4, s4) < block_sq_error(x, codes6, s6)   # ties: 6
+    sb = np.where(pick4, sb4, sb6).astype(np.uint8)
+    codes = np.where(np.repeat(pick4, BLOCK, axis=1), codes4, codes6).astype(np.uint8)
+    return codes, sb, s_t
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, s_t) -> np.ndarray:

@@ -74,14 +74,15 @@ def sigma_delta_exact(x: Fraction, quantizer: Callable[[Fraction], Fraction],
     return qs, rs
 
 
-def normalised_weight(w: np.ndarray, tensor_scale=None):
-    """Fixed-scale setup of the NVFP4 chain for an fp32 master ``w`` [R, K]:
+def normalised_weight(w: np.ndarray, tensor_scale=None, rule: str = "6"):
+    """Fixed-scale setup of the NVFP4 chain for an fp32 master ``w`` [R, K]
+(block scales by ``rule``, as in :func:`oracle.nvfp4.quantize`):
     returns (x float32 [R, K], scale bytes, s_t, block_zero mask [R, K]).
     ``tensor_scale`` (the s_t of the whole weight) lets a caller run the
     chain on a subset of rows of a larger weight."""
     w = np.asarray(w, dtype=F32)
     R, K = w.shape
-    _, sb_bytes, s_t = nvfp4.quantize(w, tensor_scale=tensor_scale)
+    _, sb_bytes, s_t = nvfp4.quantize(w, tensor_scale=tensor_scale, rule=rule)
     s_b = e4m3_decode(sb_bytes).astype(F32)
     s = (s_t * s_b).astype(F32)
     with np.errstate(divide="ignore"):
@@ -93,16 +94,18 @@ def normalised_weight(w: np.ndarray, tensor_scale=None):
     return x, sb_bytes, s_t, zero
 
 
-def sigma_delta_nvfp4(w: np.ndarray, steps: int, r0: np.ndarray = None, tensor_scale=None):
+def sigma_delta_nvfp4(w: np.ndarray, steps: int, r0: np.ndarray = None, tensor_scale=None,
+                      rule: str = "6"):
     """Run ``steps`` Sigma-Delta accesses on the fp32 master ``w`` [R, K].
 
     Returns a dict with ``codes`` (list of uint8 [R, K] per step, unpacked),
     ``residues`` (list of float32 [R, K] after each step), ``scales``
     (E4M3 bytes [R, K/16]) and ``s_t``.  ``r0`` (float32) continues a chain
     from a saved residue; default zeros.  ``tensor_scale`` as in
-    :func:`normalised_weight`.
+    :func:`normalised_weight`; ``rule="4/6"`` fixes the 4/6 block scales of
+    the loopquant page's section 2.5 listing (``block_scale_46``).
     """
-    x, sb_bytes, s_t, zero = normalised_weight(w, tensor_scale)
+    x, sb_bytes, s_t, zero = normalised_weight(w, tensor_scale, rule)
     r = np.zeros_like(x) if r0 is None else np.asarray(r0, dtype=F32).copy()
     codes_all, res_all = [], []
     for _ in range(steps):

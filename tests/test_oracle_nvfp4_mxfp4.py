@@ -222,3 +222,88 @@ def test_balance_scale_closed_form():
     assert np.allclose(t64, sig ** 0.75 / rms ** 0.25, rtol=1e-14)
     assert t32.dtype == np.float32 and u32.dtype == np.float32
     assert np.allclose(t32.astype(np.float64) * u32, 1, rtol=2e-7)
+
+
+# ------------------------------------------------ NVFP4, 4/6 block scales ----
+# loopquant page, section 2.2 (the 4/6 block scaling keeps |x/s| <= 6 with
+# the block maximum mapped to 6 or to 4) and the section 2.5 listing
+# (block_scale_46).  The choice between the two candidates is by block
+# squared error (reading adopted; ties to 6).
+
+def _e4m3_ceil_brute(y):
+    vals = F.E4M3_VALUES[:127].astype(np.float64)
+    if y <= 0:
+        return 0
+    ok = np.nonzero(vals >= y)[0]
+    return int(ok[0]) if ok.size else 126
+
+
+def test_nvfp46_exactly_representable_blocks_pick_the_exact_candidate():
+    st = np.float32(0.0625)          # candidate scales: max 4 -> 16 x st = 1, max 6 -> 16 x st = 1
+    four = [4, 2, 1, 0.5, 1.5, 3, 0, -4, -2, -1, -0.5, -1.5, -3, 0, 4, 2]      # exact at s = 1 only with max -> 4
+    six = [6, 4, 3, 2, 1.5, 1, 0.5, 0, -6, -4, -3, -2, -1.5, -1, -0.5, 0]      # exact at s = 1 only with max -> 6
+    x = np.array([four + six + [0.0] * 16], np.float32)
+    codes, scales, s_t = nvfp4.quantize(x, tensor_scale=st, rule="4/6")
+    assert s_t == st
+    assert list(scales[0]) == [0x58, 0x58, 0x00]          # E4M3 0x58 = 16; zero block: 0 (tie -> 6)
+    np.testing.assert_array_equal(F.e2m1_decode(codes[0, :32]), np.array(four + six, np.float64))
+    # the max -> 6 rule alone cannot represent the first block
+    c6, s6, _ = nvfp4.quantize(x, tensor_scale=st)
+    assert s6[0, 0] != 0x58 and not np.array_equal(F.e2m1_decode(c6[0, :16]), np.array(four, np.float64))
+
+
+def test_nvfp46_choice_follows_the_exact_block_error():
+    x = synth.heavy_tailed_f32(301, 302, (64, 256))
+    st = nvfp4.tensor_scale_from_amax(np.abs(x).max())
+    codes, scales, _ = nvfp4.quantize(x, rule="4/6")
+    xb = x.reshape(64, 16, 16).astype(np.float64)
+    picked4 = decided = 0
+    for r in range(64):
+        for b in range(16):
+            blk = xb[r, b]
+            a = np.abs(blk).max()
+            errs, bytes_ = {}, {}
+            for target in (6, 4):
+                y = np.float32(np.float32(a) / np.float32(np.float32(target) * st))
+                sb = _e4m3_ceil_brute(float(y))
+                s = np.float64(np.float32(st * np.float32(F.E4M3_VALUES[sb])))
+                v = (blk / s) if s > 0 else np.zeros(16)
+                q = np.array([F.E2M1_VALUES[np.argmin(np.abs(F.E2M1_VALUES - vi))] * 1.0 for vi in v])
+                errs[target] = float(np.sum((blk - s * q) ** 2))
+                bytes_[target] = sb
+            assert scales[r, b] in (bytes_[6], bytes_[4])
+            e6, e4 = errs[6], errs[4]
+            if abs(e6 - e4) > 1e-5 * max(e6, e4, 1e-30):
+                decided += 1
+                want = bytes_[4] if e4 < e6 else bytes_[6]
+                assert scales[r, b] == want, (r, b, e4, e6)
+                picked4 += want == bytes_[4] and bytes_[4] != bytes_[6]
+    assert decided > 900 and picked4 > 50                    # both candidates occur
+
+
+def test_nvfp46_normalised_magnitude_and_block_max_at_4():
+    x = synth.heavy_tailed_f32(303, 304, (32, 512))
+    codes, scales, st = nvfp4.quantize(x, rule="4/6")
+    s = (np.float32(st) * F.e4m3_decode(scales).astype(np.float32)).astype(np.float32)
+    rho = (np.float32(1.0) / s).astype(np.float32)
+    v = (x * np.repeat(rho, 16, axis=1)).astype(np.float32)
+    assert np.abs(v).max() <= 6.0 * (1 + 2.0 ** -20)
+    # a block that took the max -> 4 candidate with a normal scale has its
+    # maximum on code value 4
+    c6, s6, _ = nvfp4.quantize(x)
+    took4 = (scales != s6) & (scales >= 0x08)                  # normal E4M3 scale bytes
+    vals = np.abs(F.e2m1_decode(codes)).reshape(32, 32, 16)
+    xa = np.abs(x).reshape(32, 32, 16)
+    imax = xa.argmax(axis=-1)
+    vmax = np.take_along_axis(vals, imax[..., None], axis=-1)[..., 0]
+    assert took4.sum() > 20
+    np.testing.assert_array_equal(vmax[took4], 4.0)
+
+
+def test_nvfp46_total_error_not_above_max_to_6():
+    x = synth.heavy_tailed_f32(305, 306, (16, 1024))
+    c6, s6, st = nvfp4.quantize(x)
+    c46, s46, _ = nvfp4.quantize(x, rule="4/6")
+    e6 = np.sum((nvfp4.dequantize(c6, s6, st) - x) ** 2)
+    e46 = np.sum((nvfp4.dequantize(c46, s46, st) - x) ** 2)
+    assert e46 <= e6 * (1 + 1e-6) and e46 < 0.99 * e6

@@ -152,3 +152,15 @@ def test_rel_err_metric():
     y = np.array([[1.0, 0.0], [0.0, 2.0]])
     whole, row, mx = gemm.rel_err(y * (1 + 1e-4), y)
     assert abs(whole - 1e-4) < 1e-12 and abs(row - 1e-4) < 1e-12 and abs(mx - 1e-4) < 1e-12
+
+
+def test_sigma_delta_on_46_scales_keeps_the_residue_bound():
+    # the section 2.2 bound |r_k| <= d/2 = 1 holds for either 4/6 candidate,
+    # since both keep |x| <= 6 (the page's argument); the chain also averages
+    # back to x
+    w = synth.normal_f32(307, (16, 256), 0.02)
+    ref = SD.sigma_delta_nvfp4(w, 32, rule="4/6")
+    assert max(np.abs(r).max() for r in ref["residues"]) <= 1.0
+    x, _, _, _ = SD.normalised_weight(w, rule="4/6")
+    mean_q = np.mean([F.e2m1_decode(c) for c in ref["codes"]], axis=0)
+    assert np.abs(mean_q - x).max() <= 1.0 / 32 + 1e-6
