@@ -266,6 +266,23 @@ def run_extras(L, synth, np, torch, dev, stream, log):
     del xs, ws, xc, wc, y, x, w
     torch.cuda.empty_cache()
 
+    # ---------------- NVFP4 4/6 block scales on the prefill weight (10240 x 5120)
+    log("extras: NVFP4 4/6 block scales")
+    wl = synth.nvfp4_prefill()
+    wb = bf16(wl.arrays["w_bf16"])
+    del wl
+    reps = 3                                       # 3 x 105 MB > 256 MB cache
+    ws = [wb] + [wb.clone() for _ in range(reps - 1)]
+    outs = {r: [L.quantize_nvfp4(wi, rule=r) for wi in ws] for r in ("6", "4/6")}
+    nbytes = wb.numel() * (2 + 0.5 + 1 / 16)
+    fs = {"shape": list(wb.shape), "dynamic_tensor_scale": True}
+    for r, key in (("6", "max_to_6"), ("4/6", "four_six")):
+        fs[key] = _bw(_time_op(torch, stream, lambda i: L.quantize_nvfp4(ws[i % reps], rule=r, out=outs[r][i % reps]), 30),
+                      nbytes)
+    ex["nvfp4_46_quantize_w_10240x5120"] = fs
+    del ws, outs, wb
+    torch.cuda.empty_cache()
+
     # ---------------- NVFP4 decode (N 17408, K 5120, M in 1, 4, 16)
     log("extras: NVFP4 decode")
     wl = synth.nvfp4_decode()

@@ -96,9 +96,10 @@ const char* fp4q_status_str(int status) {
 
 const char* fp4q_last_error(void) { return g_last_error; }
 
-int fp4q_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+namespace {
+int quantize_nvfp4_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                         uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                        int tensor_scale_is_input, void* stream) {
+                        int tensor_scale_is_input, int four_six, void* stream, const char* what) {
   g_last_error[0] = 0;
   if (int st = check_input(x, x_dtype, rows, cols, ldx, 16, "x")) return st;
   if (!codes || !scales || !tensor_scale) return fail(FP4Q_ERR_NULL_PTR, "codes, scales and tensor_scale are required");
@@ -107,8 +108,24 @@ int fp4q_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, 
   if (tensor_scale_is_input != 0 && tensor_scale_is_input != 1) return fail(FP4Q_ERR_BAD_ARG, "tensor_scale_is_input must be 0 or 1");
   if (int st = check_device()) return st;
   return launch_status(fp4q::launch_quant_nvfp4(x, x_dtype == FP4Q_BF16, rows, cols, ldx, codes, scales,
-                                                tensor_scale, tensor_scale_is_input, as_stream(stream)),
-                       "quantize_nvfp4");
+                                                tensor_scale, tensor_scale_is_input, four_six,
+                                                as_stream(stream)),
+                       what);
+}
+}  // namespace
+
+int fp4q_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                        int tensor_scale_is_input, void* stream) {
+  return quantize_nvfp4_impl(x, x_dtype, rows, cols, ldx, codes, scales, tensor_scale, tensor_scale_is_input,
+                             0, stream, "quantize_nvfp4");
+}
+
+int fp4q_quantize_nvfp4_46(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                           int tensor_scale_is_input, void* stream) {
+  return quantize_nvfp4_impl(x, x_dtype, rows, cols, ldx, codes, scales, tensor_scale, tensor_scale_is_input,
+                             1, stream, "quantize_nvfp4_46");
 }
 
 int fp4q_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,

@@ -14,9 +14,11 @@ namespace fp4q {
 // fails).
 int device_cus();
 
+// four_six != 0: the 4/6 block scales (block maximum to 6 or to 4, whichever
+// gives the smaller block squared error)
 hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
-                              hipStream_t s);
+                              int four_six, hipStream_t s);
 // Writes max|x| into the tensor-scale cell (amax encoding).  scratch (may be
 // NULL with scratch_bytes == 0) holds per-workgroup partial maxima when it
 // is large enough; its contents are destroyed.

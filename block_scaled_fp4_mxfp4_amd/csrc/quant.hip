@@ -187,12 +187,38 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
 #endif
 constexpr int kNvUnroll = FP4Q_NV_UNROLL;
 
-template <bool BF16, bool CONTIG>
+// Squared reconstruction error of a lane's 8 elements under packed codes p
+// and total scale s, in the fixed order of the 4/6 rule:
+// d_i = fl(x_i - fl(s * value(code_i))), e_i = fl(d_i * d_i),
+// ((e0 + e1) + (e2 + e3)) + ((e4 + e5) + (e6 + e7)).
+__device__ __forceinline__ float half_block_sq_error(const float v[8], uint32_t p, float s) {
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float q0, q1;
+    switch (i) {
+      case 0: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0); q0 = q[0]; q1 = q[1]; break; }
+      case 1: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1); q0 = q[0]; q1 = q[1]; break; }
+      case 2: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2); q0 = q[0]; q1 = q[1]; break; }
+      default: { auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3); q0 = q[0]; q1 = q[1]; break; }
+    }
+    const float d0 = v[2 * i] - s * q0, d1 = v[2 * i + 1] - s * q1;
+    e[2 * i] = d0 * d0;
+    e[2 * i + 1] = d1 * d1;
+  }
+  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+}
+
+// FS: the 4/6 block scaling -- each block also tries the scale that maps its
+// maximum to 4 and keeps it when the block's squared error is strictly
+// smaller (both lanes of the pair add the two halves, so they agree).
+template <bool BF16, bool CONTIG, bool FS>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* ts, int dynamic) {
   const float st = read_tensor_scale(ts, dynamic);
   const float six_st = 6.0f * st;
+  const float four_st = 4.0f * st;
   float v[kNvUnroll][8];
   int64_t cidx[kNvUnroll];
 #pragma unroll
@@ -210,7 +236,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     if (a > 0.0f && st > 0.0f) sb = e4m3_ceil(a / six_st);
     const float s = st * e4m3_decode(sb);
     const float rho = 1.0f / s;
-    const uint32_t p = (s == 0.0f) ? 0u : encode8_scaled(v[u], rho);
+    uint32_t p = (s == 0.0f) ? 0u : encode8_scaled(v[u], rho);
+    if constexpr (FS) {
+      uint32_t sb4 = 0;
+      if (a > 0.0f && st > 0.0f) sb4 = e4m3_ceil(a / four_st);
+      const float s4 = st * e4m3_decode(sb4);
+      const float rho4 = 1.0f / s4;
+      const uint32_t p4 = (s4 == 0.0f) ? 0u : encode8_scaled(v[u], rho4);
+      const float h6 = half_block_sq_error(v[u], p, s), h4 = half_block_sq_error(v[u], p4, s4);
+      const float e6 = h6 + dpp_xor1(h6), e4 = h4 + dpp_xor1(h4);
+      if (e4 < e6) {
+        sb = sb4;
+        p = p4;
+      }
+    }
     if (cidx[u] < nchunks) {
       codes[cidx[u]] = p;
       if (!(cidx[u] & 1)) scales[cidx[u] >> 1] = (uint8_t)sb;
@@ -510,7 +549,7 @@ hipError_t launch_amax_to_cell(const void* x, int bf16, int64_t rows, int64_t co
 
 hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
-                              hipStream_t s) {
+                              int four_six, hipStream_t s) {
   const int dynamic = !ts_is_input;
   if (dynamic) {
     // the block-scale output doubles as scratch for the partial maxima; the
@@ -522,12 +561,15 @@ hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t col
   const bool contig = (ldx == cols);
   const unsigned g = grid_for(n, (int64_t)kThreads * kNvUnroll);
   auto* c32 = reinterpret_cast<uint32_t*>(codes);
-  if (bf16) {
-    if (contig) hipLaunchKernelGGL((k_quant_nvfp4<true, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
-    else hipLaunchKernelGGL((k_quant_nvfp4<true, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+  };
+  if (four_six) {
+    if (bf16) contig ? go(k_quant_nvfp4<true, true, true>) : go(k_quant_nvfp4<true, false, true>);
+    else contig ? go(k_quant_nvfp4<false, true, true>) : go(k_quant_nvfp4<false, false, true>);
   } else {
-    if (contig) hipLaunchKernelGGL((k_quant_nvfp4<false, true>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
-    else hipLaunchKernelGGL((k_quant_nvfp4<false, false>), dim3(g), dim3(kThreads), 0, s, x, n, cpr, ldx, c32, scales, ts, dynamic);
+    if (bf16) contig ? go(k_quant_nvfp4<true, true, false>) : go(k_quant_nvfp4<true, false, false>);
+    else contig ? go(k_quant_nvfp4<false, true, false>) : go(k_quant_nvfp4<false, false, false>);
   }
   return hipGetLastError();
 }

@@ -41,6 +41,7 @@ _SIGS = {
     "fp4q_status_str": ([_i], ctypes.c_char_p),
     "fp4q_last_error": ([], ctypes.c_char_p),
     "fp4q_quantize_nvfp4": ([_p, _i, _l, _l, _l, _p, _p, _p, _i, _p], _i),
+    "fp4q_quantize_nvfp4_46": ([_p, _i, _l, _l, _l, _p, _p, _p, _i, _p], _i),
     "fp4q_quantize_mxfp4": ([_p, _i, _l, _l, _l, _p, _i, _p, _p, _p], _i),
     "fp4q_hadamard32_scale": ([_p, _i, _l, _l, _l, _p, _p, _l, _p], _i),
     "fp4q_balance_scale": ([_p, _i, _l, _l, _l, _p, _i, _l, _l, ctypes.c_double, _p, _p, _p], _i),
@@ -98,11 +99,15 @@ def abi_version() -> int:
 # ---------------------------------------------------------------- quant ----
 
 def quantize_nvfp4(x: torch.Tensor, tensor_scale: Optional[torch.Tensor] = None,
-                   out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+                   out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                   rule: str = "6"):
     """NVFP4-quantize ``x`` (fp32 or bf16 [rows, cols]).  Returns
     (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], tensor_scale
     fp32 [1]).  With ``tensor_scale`` given (fp32 [1] device tensor) it is
-    used as s_t; otherwise s_t = max|x| / 1536 is computed on the device."""
+    used as s_t; otherwise s_t = max|x| / 1536 is computed on the device.
+    ``rule="4/6"`` selects the 4/6 block scales (fp4q_quantize_nvfp4_46)."""
+    if rule not in ("6", "4/6"):
+        raise ValueError(f"rule must be '6' or '4/6', not {rule!r}")
     rows, cols, ld = _rows_cols_ld(x)
     dev = x.device
     if out is None:
@@ -116,8 +121,9 @@ def quantize_nvfp4(x: torch.Tensor, tensor_scale: Optional[torch.Tensor] = None,
         if ts.data_ptr() != tensor_scale.data_ptr():
             ts.copy_(tensor_scale)
         is_input = 1
-    _check(lib.fp4q_quantize_nvfp4(_ptr(x), _dtype_code(x), rows, cols, ld, _ptr(codes), _ptr(scales),
-                                   _ptr(ts), is_input, _stream(dev)), "quantize_nvfp4")
+    fn = lib.fp4q_quantize_nvfp4 if rule == "6" else lib.fp4q_quantize_nvfp4_46
+    _check(fn(_ptr(x), _dtype_code(x), rows, cols, ld, _ptr(codes), _ptr(scales),
+              _ptr(ts), is_input, _stream(dev)), "quantize_nvfp4")
     return codes, scales, ts
 
 

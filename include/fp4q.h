@@ -98,6 +98,25 @@ int fp4q_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, 
                         int tensor_scale_is_input, void* stream);
 
 /*
+ * NVFP4 quantization with 4/6 block scales.  [LQ] section 2.2 (paragraph
+ * applying the residue bound to the signed E2M1 code book: the 4/6 block
+ * scaling keeps |x / s| <= 6 whether the rounded-up E4M3 candidate maps the
+ * block maximum to 6 or to 4) and the section 2.5 listing (block_scale_46).
+ * Per 16-block both candidates are encoded exactly as in
+ * fp4q_quantize_nvfp4, with 6 * s_t replaced by 4 * s_t for the second:
+ *     s_b(c) = ceil_E4M3(a_b / (c * s_t)),  c in {6, 4}
+ * and the block keeps candidate 4 only if its squared error is strictly
+ * smaller, both in binary32 in this fixed order:
+ *     d_i = x_i - (s(c) * value(code_i)),  e_i = d_i * d_i
+ *     E = [((e0+e1)+(e2+e3))+((e4+e5)+(e6+e7))] + [same over elements 8..15]
+ * Arguments, buffers, scratch use and errors as for fp4q_quantize_nvfp4;
+ * the outputs feed every NVFP4 consumer (GEMMs, Sigma-Delta) unchanged.
+ */
+int fp4q_quantize_nvfp4_46(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                           int tensor_scale_is_input, void* stream);
+
+/*
  * MXFP4 quantization with the optional online transform.  [MQ] background
  * box "MXFP4 micro-scaling format" (OCP MXFP4: 32-element blocks, E8M0
  * power-of-two scale, E2M1 elements) and "Method steps" 1-3 (activations

@@ -55,6 +55,8 @@ def test_validation_happens_before_any_device_work(fp4q):
     assert L.fp4q_quantize_nvfp4(P(0x1002), 1, 4, 32, 32, fake16, fake, fake, 0, None) == 3   # misaligned x
     assert L.fp4q_quantize_nvfp4(fake16, 7, 4, 32, 32, fake16, fake, fake, 0, None) == 4      # dtype
     assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, fake, fake, 2, None) == 5      # flag
+    assert L.fp4q_quantize_nvfp4_46(fake16, 1, 4, 24, 24, fake16, fake, fake, 0, None) == 2   # cols % 16
+    assert L.fp4q_quantize_nvfp4_46(None, 1, 4, 32, 32, fake16, fake, fake, 0, None) == 1
     assert L.fp4q_quantize_mxfp4(fake16, 1, 4, 48, 48, None, 0, fake16, fake, None) == 2      # cols % 32
     assert L.fp4q_quantize_mxfp4(fake16, 1, 4, 64, 64, None, 3, fake16, fake, None) == 5
     assert L.fp4q_gemm_w4a4(5, fake16, fake16, fake, fake16, fake16, fake, 4, 4, 128, fake16, 4, None) == 4

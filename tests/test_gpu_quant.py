@@ -13,15 +13,15 @@ pytestmark = pytest.mark.gpu
 F32 = np.float32
 
 
-def _nv_check(x_f32_host, x_dev, tensor_scale=None, rows=None):
+def _nv_check(x_f32_host, x_dev, tensor_scale=None, rows=None, rule="6"):
     L = fp4q()
     ts_in = None if tensor_scale is None else dev_f32(np.array([tensor_scale], F32))
-    codes, scales, ts = L.quantize_nvfp4(x_dev, tensor_scale=ts_in)
+    codes, scales, ts = L.quantize_nvfp4(x_dev, tensor_scale=ts_in, rule=rule)
     codes, scales, ts = host(codes), host(scales), host(ts)
     st_ref = ONV.tensor_scale_from_amax(np.abs(x_f32_host).max()) if tensor_scale is None else F32(tensor_scale)
     assert ts[0] == st_ref, (ts[0], st_ref)
     sel = np.arange(x_f32_host.shape[0]) if rows is None else rows
-    c_ref, s_ref, _ = ONV.quantize(x_f32_host[sel], tensor_scale=st_ref)
+    c_ref, s_ref, _ = ONV.quantize(x_f32_host[sel], tensor_scale=st_ref, rule=rule)
     assert_bytes_equal(scales[sel], s_ref, "nvfp4 scales")
     assert_bytes_equal(codes[sel], packed(c_ref), "nvfp4 codes")
 
@@ -88,6 +88,63 @@ def test_nvfp4_prefill_full_size_sampled_rows():
         b = wl.arrays[name]
         xf = OF.bf16_bits_to_f32(b)
         _nv_check(xf, dev_bf16(b), rows=sample_rows(b.shape[0], seed=hash(name) % 1000))
+
+
+def test_nvfp46_tiny_ragged_strided_and_static():
+    # 4/6 block scales: same inputs as the max -> 6 tests, bit-exact
+    wl = synth.nvfp4_tiny()
+    for name in ("x", "w"):
+        a = wl.arrays[name]
+        _nv_check(a, dev_f32(a), rule="4/6")
+    x = synth.heavy_tailed_f32(401, 402, (37, 96))
+    xb = synth.f32_to_bf16_bits(x)
+    xf = OF.bf16_bits_to_f32(xb)
+    full = dev_bf16(xb)
+    _nv_check(np.ascontiguousarray(xf[:, :80]), full[:, :80], rule="4/6")
+    _nv_check(xf, full, tensor_scale=F32(0.0123), rule="4/6")
+    _nv_check(x, dev_f32(x), rule="4/6")
+
+
+def test_nvfp46_edge_values_and_exact_blocks():
+    x = synth.normal_f32(403, (8, 64))
+    x[0, :16] = 0.0                      # zero block
+    x[1, :] = -0.0
+    x[1, 3] = 1e-3
+    x[2, :16] = np.float32(3e38)         # huge block (errors overflow to inf: tie -> 6)
+    x[3, :16] = np.float32(1e-42)        # subnormal block
+    x[4, 5] = np.float32(-7e-45)
+    _nv_check(x, dev_f32(x), rule="4/6")
+    # blocks exactly representable under exactly one candidate (s_t = 1/16)
+    four = [4, 2, 1, 0.5, 1.5, 3, 0, -4, -2, -1, -0.5, -1.5, -3, 0, 4, 2]
+    six = [6, 4, 3, 2, 1.5, 1, 0.5, 0, -6, -4, -3, -2, -1.5, -1, -0.5, 0]
+    e = np.array([four + six] * 4, F32)
+    _nv_check(e, dev_f32(e), tensor_scale=F32(0.0625), rule="4/6")
+
+
+def test_nvfp46_prefill_full_size_sampled_rows():
+    wl = synth.nvfp4_prefill()
+    for name in ("x_bf16", "w_bf16"):
+        b = wl.arrays[name]
+        xf = OF.bf16_bits_to_f32(b)
+        _nv_check(xf, dev_bf16(b), rows=sample_rows(b.shape[0], seed=hash(name) % 1000 + 7), rule="4/6")
+
+
+def test_sigma_delta_on_46_scales():
+    # the looped core's chain with the 4/6 block scales of the section 2.5
+    # listing: codes and residues bit-exact over several steps
+    L = fp4q()
+    w = synth.normal_f32(404, (96, 768), 0.02)
+    wd = dev_f32(w)
+    _, sc, ts = L.quantize_nvfp4(wd, rule="4/6")
+    codes = torch.empty((96, 384), dtype=torch.uint8, device="cuda:0")
+    res = torch.zeros_like(wd)
+    seg = [{"w": wd, "scales": sc, "tensor_scale": ts, "residue": res, "codes": codes}]
+    ref = OSD.sigma_delta_nvfp4(w, 5, rule="4/6")
+    assert_bytes_equal(host(sc), ref["scales"], "4/6 scales")
+    for k in range(5):
+        L.sigma_delta_requant(seg, steps=1)
+        assert_bytes_equal(host(codes), packed(ref["codes"][k]), f"codes step {k + 1}")
+        assert_bytes_equal(host(res).view(np.uint32), ref["residues"][k].view(np.uint32), f"residue step {k + 1}")
 
 
 def test_nvfp4_dynamic_large_tensor():
