@@ -161,6 +161,23 @@ def e4m3_ceil(y: np.ndarray) -> np.ndarray:
     return idx.astype(np.uint8)
 
 
+def e4m3_round_nearest(y: np.ndarray) -> np.ndarray:
+    """Nearest non-negative finite E4M3 value to y (y >= 0), as a byte; ties
+    go to the even byte (even mantissa); above 448 saturates to 448 (0x7E).
+    Brute force over the 127 non-negative finite codes, like
+    :func:`e4m3_ceil`."""
+    y = np.asarray(y, dtype=np.float64)
+    assert not np.any(np.isnan(y)) and np.all(y >= 0)
+    table = E4M3_VALUES[:127]
+    hi = np.minimum(np.searchsorted(table, y, side="left"), 126)   # first table[i] >= y
+    lo = np.maximum(hi - 1, 0)
+    d_hi = table[hi] - y
+    d_lo = y - table[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    out = np.where(pick_lo & (hi > 0) & (y < table[126]), lo, hi)
+    return out.astype(np.uint8)
+
+
 # ---------------------------------------------------------------- E8M0 ----
 
 def e8m0_decode(bytes_: np.ndarray) -> np.ndarray:

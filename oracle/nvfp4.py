@@ -17,6 +17,9 @@ Definition followed:
 
 * loopquant page, section 2.2 and the section 2.5 listing: the 4/6 block
   scaling (``rule="4/6"`` of :func:`quantize`).
+* "Why Gated DeltaNet Survives 4-Bit Quantization", fused-GEMM global-scale
+  box and pipeline step (2): one shared tensor scale for the members of a
+  fused GEMM (:func:`harmonize`).
 
 The order of the fp32 operations is the reading this project takes where the
 pages are silent (recorded in the design notes): every step is a single
@@ -34,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e2m1_round, e2m1_decode, e4m3_ceil, e4m3_decode
+from .formats import e2m1_round, e2m1_decode, e4m3_ceil, e4m3_decode, e4m3_round_nearest
 
 BLOCK = 16
 F32 = np.float32
@@ -150,3 +153,30 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, s_t) -> np.ndarray:
     q = e2m1_decode(codes)
     sb = np.repeat(e4m3_decode(scales), BLOCK, axis=1)
     return q * sb * np.float64(F32(s_t))
+
+
+def harmonize(scales, tensor_scales):
+    """One shared tensor scale for the members of a fused projection.
+
+    "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the
+    Recurrent Half of a Hybrid 27B LLM", background box on fused GEMMs and
+    the global-scale mismatch, and step (2) of its pipeline: the members of a
+    fused NVFP4 GEMM are rewritten to one shared global scale (the largest
+    member scale, the one the fused GEMM uses), each member's ratio folded
+    into its E4M3 block scales; codes are unchanged and the re-rounding is at
+    most half an E4M3 step (the page reports <= 6.2%).  Reading: the scale is
+    the decode multiplier s_t of this module, so every ratio is <= 1 and no
+    block scale can pass 448; a block scale that falls below half the
+    smallest E4M3 subnormal becomes 0.
+        s_t  = max_i s_t,i
+        r_i  = fl(s_t,i / s_t)                 (1 if s_t == 0)
+        s_b' = nearest_E4M3( fl(s_b * r_i) )   (ties to even)
+    Returns (list of new scale-byte arrays, s_t)."""
+    sts = [F32(t) for t in tensor_scales]
+    st = max(sts)
+    out = []
+    for sb, ti in zip(scales, sts):
+        r = F32(ti / st) if st > 0 else F32(1.0)
+        prod = (e4m3_decode(sb).astype(F32) * r).astype(F32)
+        out.append(e4m3_round_nearest(prod.astype(np.float64)))
+    return out, st

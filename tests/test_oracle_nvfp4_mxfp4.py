@@ -307,3 +307,65 @@ def test_nvfp46_total_error_not_above_max_to_6():
     e6 = np.sum((nvfp4.dequantize(c6, s6, st) - x) ** 2)
     e46 = np.sum((nvfp4.dequantize(c46, s46, st) - x) ** 2)
     assert e46 <= e6 * (1 + 1e-6) and e46 < 0.99 * e6
+
+
+# ------------------------------------- fused-projection scale harmonization ----
+# "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the
+# Recurrent Half of a Hybrid 27B LLM", fused-GEMM global-scale box and
+# pipeline step (2): one shared global scale per fused group, member ratios
+# folded into the E4M3 block scales, re-rounding at most ~6.2%.
+
+def test_e4m3_round_nearest_matches_torch_and_ties_to_even():
+    vals = F.E4M3_VALUES[:127]
+    mids = (vals[:-1] + vals[1:]) / 2                       # exact midpoints (float64)
+    rng = np.random.default_rng(311)
+    ys = np.concatenate([vals, mids, rng.uniform(0, 448, 20000), 2.0 ** rng.uniform(-14, 8.8, 20000)])
+    ys = np.minimum(ys.astype(np.float32).astype(np.float64), 448.0)
+    got = F.e4m3_round_nearest(ys)
+    want = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, want)
+    # ties: the midpoint between bytes 0x40 (2.0) and 0x41 (2.25) goes to 0x40, 0x41..0x42 to 0x42
+    assert F.e4m3_round_nearest(np.array([2.125]))[0] == 0x40
+    assert F.e4m3_round_nearest(np.array([2.375]))[0] == 0x42
+
+
+def test_harmonize_identity_power_of_two_and_bound():
+    rng = np.random.default_rng(312)
+    sb = rng.integers(0x08, 0x7F, (64, 32)).astype(np.uint8)           # normal E4M3 scales
+    (same,), st = nvfp4.harmonize([sb], [np.float32(0.01)])
+    np.testing.assert_array_equal(same, sb)
+    # ratio 1/2: every normal scale >= 2^-5 halves exactly
+    big = np.where(F.e4m3_decode(sb) >= 2.0 ** -5, sb, 0x30).astype(np.uint8)
+    out, st = nvfp4.harmonize([big, big], [np.float32(0.5), np.float32(1.0)])
+    np.testing.assert_array_equal(F.e4m3_decode(out[0]), F.e4m3_decode(big) / 2)
+    np.testing.assert_array_equal(out[1], big)
+    assert st == np.float32(1.0)
+    # worst ratio of the page (2.81x): normal results within half an E4M3 step
+    out, st = nvfp4.harmonize([sb], [np.float32(1.0 / 2.81)])
+    out2, _ = nvfp4.harmonize([sb, sb], [np.float32(1.0 / 2.81), np.float32(1.0)])
+    np.testing.assert_array_equal(out2[0], F.e4m3_round_nearest(
+        (F.e4m3_decode(sb).astype(np.float32) * np.float32(np.float32(1.0 / 2.81) / np.float32(1.0))).astype(np.float64)))
+    exact = F.e4m3_decode(sb) * np.float64(np.float32(np.float32(1.0 / 2.81) / np.float32(1.0)))
+    got = F.e4m3_decode(out2[0])
+    normal = exact >= 2.0 ** -6
+    assert np.all(np.abs(got[normal] - exact[normal]) <= exact[normal] / 16 * (1 + 1e-9))
+
+
+def test_harmonized_fused_gemm_matches_separate_gemms():
+    # the page's probe: a fused GEMM that takes the larger member scale
+    # without rescaling is badly wrong; after harmonization it matches the
+    # members' own GEMMs up to the re-rounding
+    from oracle import gemm as G
+    x = synth.heavy_tailed_f32(313, 314, (32, 256))
+    w1 = synth.normal_f32(315, (48, 256), 0.02)
+    w2 = synth.normal_f32(316, (48, 256), 0.02 / 2.75)          # member scales differ 2.75x
+    cx, sx, tx = nvfp4.quantize(x)
+    c1, s1, t1 = nvfp4.quantize(w1)
+    c2, s2, t2 = nvfp4.quantize(w2)
+    ref = np.concatenate([G.w4a4_nvfp4(cx, sx, tx, c1, s1, t1), G.w4a4_nvfp4(cx, sx, tx, c2, s2, t2)], axis=1)
+    cw = np.concatenate([c1, c2])
+    naive = G.w4a4_nvfp4(cx, sx, tx, cw, np.concatenate([s1, s2]), max(t1, t2))
+    (h1, h2), st = nvfp4.harmonize([s1, s2], [t1, t2])
+    fused = G.w4a4_nvfp4(cx, sx, tx, cw, np.concatenate([h1, h2]), st)
+    assert G.rel_err(naive, ref)[0] > 0.3
+    assert G.rel_err(fused, ref)[0] < 0.03
