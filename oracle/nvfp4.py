@@ -171,12 +171,18 @@ def harmonize(scales, tensor_scales):
         s_t  = max_i s_t,i
         r_i  = fl(s_t,i / s_t)                 (1 if s_t == 0)
         s_b' = nearest_E4M3( fl(s_b * r_i) )   (ties to even)
+    Bytes that are not a non-negative finite E4M3 value (sign bit set, or
+    NaN), which no quantizer here writes, are left as they are.  After the
+    rewrite every member decodes with s_t.
     Returns (list of new scale-byte arrays, s_t)."""
     sts = [F32(t) for t in tensor_scales]
     st = max(sts)
     out = []
     for sb, ti in zip(scales, sts):
+        sb = np.asarray(sb, dtype=np.uint8)
         r = F32(ti / st) if st > 0 else F32(1.0)
-        prod = (e4m3_decode(sb).astype(F32) * r).astype(F32)
-        out.append(e4m3_round_nearest(prod.astype(np.float64)))
+        valid = sb <= 0x7E
+        dec = e4m3_decode(np.where(valid, sb, 0).astype(np.uint8)).astype(F32)
+        prod = (dec * r).astype(F32)
+        out.append(np.where(valid, e4m3_round_nearest(prod.astype(np.float64)), sb).astype(np.uint8))
     return out, st

@@ -351,6 +351,18 @@ def test_harmonize_identity_power_of_two_and_bound():
     assert np.all(np.abs(got[normal] - exact[normal]) <= exact[normal] / 16 * (1 + 1e-9))
 
 
+def test_harmonize_leaves_invalid_bytes_and_zero_scales():
+    sb = np.array([[0x00, 0x7F, 0x80, 0xFE, 0xFF, 0x01, 0x7E]], dtype=np.uint8)
+    (out,), st = nvfp4.harmonize([sb], [np.float32(0.25)])
+    np.testing.assert_array_equal(out, sb)                       # ratio 1
+    (out, _), st = nvfp4.harmonize([sb, sb], [np.float32(0.25), np.float32(1.0)])
+    # 0 -> 0; invalid bytes untouched; 2^-9/4 -> 0; 448/4 = 112 = 1.75 * 2^6 -> 0x6E
+    np.testing.assert_array_equal(out, np.array([[0x00, 0x7F, 0x80, 0xFE, 0xFF, 0x00, 0x6E]], np.uint8))
+    # all members zero: the shared scale is 0 and nothing changes
+    out, st = nvfp4.harmonize([sb, sb], [np.float32(0.0), np.float32(0.0)])
+    assert st == 0 and all(np.array_equal(o, sb) for o in out)
+
+
 def test_harmonized_fused_gemm_matches_separate_gemms():
     # the page's probe: a fused GEMM that takes the larger member scale
     # without rescaling is badly wrong; after harmonization it matches the
