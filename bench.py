@@ -283,6 +283,34 @@ def run_extras(L, synth, np, torch, dev, stream, log):
     del ws, outs, wb
     torch.cuda.empty_cache()
 
+    # ---------------- shared tensor scale for a fused projection (members of
+    # 10240 and 5120 rows, K 5120, member scales 1.82x apart): the member
+    # with the smaller scale (10240 x 320 scale bytes) is rewritten in place.
+    # Every call first restores the member cells (else the next call is the
+    # identity and exits early); the restore alone is timed beside it.
+    log("extras: fused-member scale harmonization")
+    sa = torch.from_numpy(synth.uint8_bytes(430, (10240, 320), 0, 0x7F)).to(dev)
+    sb = torch.from_numpy(synth.uint8_bytes(431, (5120, 320), 0, 0x7F)).to(dev)
+    orig = torch.tensor([0.0021, 0.0021 * 1.82], dtype=torch.float32, device=dev)
+    cells = orig.clone()
+    shared = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def hz(i):
+        cells.copy_(orig)
+        L.harmonize_nvfp4([sa, sb], [cells[0:1], cells[1:2]], shared=shared)
+
+    both = _time_op(torch, stream, hz, 50)
+    reset = _time_op(torch, stream, lambda i: cells.copy_(orig), 50)
+    net = max(both["median_ms"] - reset["median_ms"], 1e-6)
+    ex["nvfp4_harmonize_fused_15360x5120"] = {
+        "members": [[10240, 5120], [5120, 5120]], "scale_ratio": 1.82,
+        "with_cell_restore": {k: round(v, 4) for k, v in both.items()},
+        "cell_restore_only": {k: round(v, 4) for k, v in reset.items()},
+        "net_ms": round(net, 4), "bytes_rewritten": 2 * sa.numel(),
+        "GBps_net": round(2 * sa.numel() / (net * 1e-3) / 1e9, 1)}
+    del sa, sb
+    torch.cuda.empty_cache()
+
     # ---------------- NVFP4 decode (N 17408, K 5120, M in 1, 4, 16)
     log("extras: NVFP4 decode")
     wl = synth.nvfp4_decode()

@@ -196,6 +196,39 @@ int fp4q_sigma_delta_requant(const fp4q_sd_segment* segs, int nseg, int steps,
                        "sigma_delta_requant");
 }
 
+int fp4q_harmonize_nvfp4(const fp4q_nv_member* members, int n_members,
+                         float* shared_tensor_scale, void* stream) {
+  g_last_error[0] = 0;
+  if (!members || !shared_tensor_scale) return fail(FP4Q_ERR_NULL_PTR, "members or shared_tensor_scale is NULL");
+  if (n_members < 1 || n_members > 16) return fail(FP4Q_ERR_BAD_ARG, "n_members must be in [1, 16]");
+  for (int i = 0; i < n_members; ++i) {
+    const fp4q_nv_member& m = members[i];
+    if (!m.scales || !m.tensor_scale) return fail(FP4Q_ERR_NULL_PTR, "member %d has a NULL pointer", i);
+    if (m.rows <= 0 || m.cols <= 0 || m.cols % 16) return fail(FP4Q_ERR_BAD_SHAPE, "member %d: bad shape", i);
+    if (m.rows * (m.cols / 16) > (int64_t(1) << 36)) return fail(FP4Q_ERR_BAD_SHAPE, "member %d: too large", i);
+  }
+  // every scale range must be disjoint from the other scale ranges and
+  // from every fp32 cell the kernels read or write
+  auto lo = [&](int i) { return reinterpret_cast<uintptr_t>(members[i].scales); };
+  auto hi = [&](int i) { return lo(i) + (uintptr_t)(members[i].rows * (members[i].cols / 16)); };
+  auto hits = [&](int i, const void* cell) {
+    const uintptr_t c = reinterpret_cast<uintptr_t>(cell);
+    return c + sizeof(float) > lo(i) && c < hi(i);
+  };
+  for (int i = 0; i < n_members; ++i) {
+    if (hits(i, shared_tensor_scale)) return fail(FP4Q_ERR_BAD_ARG, "member %d: scales overlap the shared cell", i);
+    for (int j = 0; j < n_members; ++j) {
+      if (hits(i, members[j].tensor_scale))
+        return fail(FP4Q_ERR_BAD_ARG, "member %d: scales overlap the tensor scale of member %d", i, j);
+      if (j != i && lo(i) < hi(j) && lo(j) < hi(i))
+        return fail(FP4Q_ERR_BAD_ARG, "members %d and %d: scale ranges overlap", i, j);
+    }
+  }
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_harmonize_nvfp4(members, n_members, shared_tensor_scale, as_stream(stream)),
+                       "harmonize_nvfp4");
+}
+
 int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
                    int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream) {

@@ -77,6 +77,18 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// Nearest E4M3 byte to a binary32 f in [0, 448], ties to the even byte.
+// Below 2^-6 the E4M3 grid is m * 2^-9 (m = 0..8; m = 8 is byte 0x08, the
+// smallest normal), so the byte is the integer nearest to f * 2^9.  Above,
+// the three leading mantissa bits are rounded to nearest-even on the
+// binary32 pattern; a carry moves into the exponent field, and the exponent
+// bias changes from 127 to 7 (120 << 3 = 960 in byte units).
+__device__ __forceinline__ uint32_t e4m3_round_nearest(float f) {
+  if (f < 0.015625f) return (uint32_t)__builtin_rintf(f * 512.0f);
+  const uint32_t u = __float_as_uint(f);
+  return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
+}
+
 // ---------------------------------------------------------------- E8M0 ----
 
 // MXFP4 block exponent e = floor(log2 a) - 2 clamped to [-127, 127] for a

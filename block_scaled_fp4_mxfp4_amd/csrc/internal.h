@@ -35,6 +35,7 @@ hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K,
                                 float* t_out, float* u_out, hipStream_t s);
 hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
                               int64_t bank_stride, hipStream_t s);
+hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* shared, hipStream_t s);
 
 hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,

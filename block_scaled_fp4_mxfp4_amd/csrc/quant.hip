@@ -516,6 +516,96 @@ __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int
   }
 }
 
+// ------------------------------------------ fused-member harmonization ----
+// One shared tensor scale for the members of a fused NVFP4 GEMM: s_t is the
+// largest member scale; member i's block scales become the E4M3 value
+// nearest to fl(s_b * fl(s_t,i / s_t)), codes untouched.  Bytes that are
+// not a non-negative finite E4M3 value are left as they are.  A member with
+// ratio 1 is left as it is (the rewrite is the identity there).
+//
+// Work split: a member's bytes are a 16-byte aligned body of 16-byte chunks
+// plus at most 30 edge bytes (before the first aligned address and after
+// the last whole chunk).  Item c < nchunk is body chunk c; item nchunk is
+// the edge, done byte by byte by one thread.
+
+constexpr int kHzMaxMem = 16;
+
+struct HzArgs {
+  uint8_t* scales[kHzMaxMem];
+  const float* ts[kHzMaxMem];
+  int64_t nbytes[kHzMaxMem];
+  int32_t head[kHzMaxMem];           // bytes before the first 16-byte aligned address
+  int32_t wg_start[kHzMaxMem + 1];
+  int32_t n;
+};
+
+#ifndef FP4Q_HZ_UNROLL
+#define FP4Q_HZ_UNROLL 2        // 16-byte chunks per thread
+#endif
+constexpr int kHzUnroll = FP4Q_HZ_UNROLL;
+
+__device__ __forceinline__ uint32_t harmonize_byte(uint32_t b, float r) {
+  return b <= 0x7Eu ? e4m3_round_nearest(e4m3_decode(b) * r) : b;
+}
+
+__device__ __forceinline__ uint32_t harmonize_word(uint32_t w, float r) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o |= harmonize_byte((w >> (8 * j)) & 0xFFu, r) << (8 * j);
+  return o;
+}
+
+__global__ __launch_bounds__(kThreads) void k_harmonize(const HzArgs a) {
+  int m = 0;
+  while (m + 1 < a.n && (int)blockIdx.x >= a.wg_start[m + 1]) ++m;
+  float st = 0.0f;
+  for (int i = 0; i < a.n; ++i) st = fmaxf(st, *a.ts[i]);
+  const float r = st > 0.0f ? *a.ts[m] / st : 1.0f;
+  if (r == 1.0f) return;                               // uniform over the workgroup
+  uint8_t* __restrict__ p = a.scales[m];
+  const int64_t nb = a.nbytes[m], head = a.head[m];
+  const int64_t nchunk = (nb - head) >> 4;
+  const int64_t wg = (int64_t)blockIdx.x - a.wg_start[m];
+  auto* body = reinterpret_cast<uint4*>(p + head);
+  int64_t c[kHzUnroll];
+  bool edge = false;
+#pragma unroll
+  for (int u = 0; u < kHzUnroll; ++u) {
+    c[u] = (wg * kHzUnroll + u) * kThreads + threadIdx.x;
+    edge |= c[u] == nchunk;
+  }
+  if (nchunk > 0) {                                     // uniform
+    uint4 v[kHzUnroll];
+#pragma unroll
+    for (int u = 0; u < kHzUnroll; ++u) v[u] = body[clamp_chunk(c[u], nchunk)];
+#pragma unroll
+    for (int u = 0; u < kHzUnroll; ++u) {
+      if (c[u] < nchunk) {
+        uint4 o;
+        o.x = harmonize_word(v[u].x, r);
+        o.y = harmonize_word(v[u].y, r);
+        o.z = harmonize_word(v[u].z, r);
+        o.w = harmonize_word(v[u].w, r);
+        body[c[u]] = o;
+      }
+    }
+  }
+  if (edge) {                                           // one thread of the member
+    for (int64_t i = 0; i < head; ++i) p[i] = (uint8_t)harmonize_byte(p[i], r);
+    for (int64_t i = head + nchunk * 16; i < nb; ++i) p[i] = (uint8_t)harmonize_byte(p[i], r);
+  }
+}
+
+// After every member is rewritten: all member cells and the shared cell
+// take the shared scale (one thread, so aliased cells are harmless).
+__global__ void k_harmonize_cells(const HzArgs a, float* shared) {
+  if (threadIdx.x != 0) return;
+  float st = 0.0f;
+  for (int i = 0; i < a.n; ++i) st = fmaxf(st, *a.ts[i]);
+  for (int i = 0; i < a.n; ++i) *const_cast<float*>(a.ts[i]) = st;
+  *shared = st;
+}
+
 inline unsigned grid_for(int64_t items, int64_t per_block) {
   return (unsigned)((items + per_block - 1) / per_block);
 }
@@ -661,6 +751,29 @@ hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* shared, hipStream_t s) {
+  HzArgs a = {};
+  a.n = n;
+  int32_t wg = 0;
+  for (int i = 0; i < n; ++i) {
+    a.scales[i] = mem[i].scales;
+    a.ts[i] = mem[i].tensor_scale;
+    a.nbytes[i] = mem[i].rows * (mem[i].cols / 16);
+    const int64_t mis = (int64_t)(reinterpret_cast<uintptr_t>(mem[i].scales) & 15u);
+    const int64_t head = mis ? 16 - mis : 0;
+    a.head[i] = (int32_t)(head < a.nbytes[i] ? head : a.nbytes[i]);
+    a.wg_start[i] = wg;
+    const int64_t items = ((a.nbytes[i] - a.head[i]) >> 4) + 1;      // body chunks + the edge
+    wg += (int32_t)grid_for(items, (int64_t)kThreads * kHzUnroll);
+  }
+  a.wg_start[n] = wg;
+  hipLaunchKernelGGL(k_harmonize, dim3(wg), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_harmonize_cells, dim3(1), dim3(64), 0, s, a, shared);
+  return hipGetLastError();
 }
 
 }  // namespace fp4q

@@ -36,6 +36,10 @@ class SdSegment(ctypes.Structure):
                 ("codes", _p), ("rows", _l), ("cols", _l)]
 
 
+class NvMember(ctypes.Structure):
+    _fields_ = [("scales", _p), ("tensor_scale", _p), ("rows", _l), ("cols", _l)]
+
+
 _SIGS = {
     "fp4q_abi_version": ([], _i),
     "fp4q_status_str": ([_i], ctypes.c_char_p),
@@ -46,6 +50,7 @@ _SIGS = {
     "fp4q_hadamard32_scale": ([_p, _i, _l, _l, _l, _p, _p, _l, _p], _i),
     "fp4q_balance_scale": ([_p, _i, _l, _l, _l, _p, _i, _l, _l, ctypes.c_double, _p, _p, _p], _i),
     "fp4q_sigma_delta_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, _p], _i),
+    "fp4q_harmonize_nvfp4": ([ctypes.POINTER(NvMember), _i, _p, _p], _i),
     "fp4q_gemm_w4a4": ([_i, _p, _p, _p, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_gemm_w4a16": ([_p, _l, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_linear_w4a4": ([_p, _l, _p, _i, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
@@ -181,6 +186,25 @@ def sigma_delta_requant(segments: Sequence[dict], steps: int = 1, bank_stride: i
                            s["residue"].data_ptr(), s["codes"].data_ptr(), w.shape[0], w.shape[1])
     _check(lib.fp4q_sigma_delta_requant(arr, len(segments), int(steps), int(bank_stride), _stream(dev)),
            "sigma_delta_requant")
+
+
+def harmonize_nvfp4(scales: Sequence[torch.Tensor], tensor_scales: Sequence[torch.Tensor],
+                    shared: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Give the members of a fused NVFP4 GEMM one shared tensor scale.  Each
+    member is its E4M3 block scales (uint8 [rows, cols/16], rewritten in
+    place) and its fp32 [1] tensor scale (overwritten with the shared one).
+    Returns the shared scale (fp32 [1]; ``shared`` if given)."""
+    if len(scales) != len(tensor_scales):
+        raise ValueError("one tensor scale per member")
+    arr = (NvMember * len(scales))()
+    for i, (sb, ts) in enumerate(zip(scales, tensor_scales)):
+        if sb.dtype != torch.uint8 or sb.dim() != 2 or not sb.is_contiguous():
+            raise ValueError("member scales must be contiguous uint8 [rows, cols/16]")
+        arr[i] = NvMember(sb.data_ptr(), ts.data_ptr(), sb.shape[0], sb.shape[1] * 16)
+    dev = scales[0].device if len(scales) else torch.device("cuda")
+    out = torch.empty(1, dtype=torch.float32, device=dev) if shared is None else shared
+    _check(lib.fp4q_harmonize_nvfp4(arr, len(scales), _ptr(out), _stream(dev)), "harmonize_nvfp4")
+    return out
 
 
 # ----------------------------------------------------------------- GEMM ----

@@ -44,6 +44,11 @@ def normal_f32(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
     return (rng.standard_normal(shape) * sigma).astype(np.float32)
 
 
+def uint8_bytes(seed: int, shape, lo: int = 0, hi: int = 256) -> np.ndarray:
+    """Uniform random bytes in [lo, hi)."""
+    return np.random.default_rng(seed).integers(lo, hi, shape, dtype=np.uint8)
+
+
 def outlier_columns(seed: int, k: int, count: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return np.sort(rng.choice(k, size=count, replace=False))

@@ -202,6 +202,42 @@ int fp4q_sigma_delta_requant(const fp4q_sd_segment* segs, int nseg, int steps,
                              int64_t bank_stride_bytes, void* stream);
 
 /*
+ * One member of a fused NVFP4 GEMM (weights quantized separately and
+ * concatenated along N).  The ARRAY of members lives in HOST memory; the
+ * pointers inside it are device pointers.
+ *   scales:       [rows][cols/16] E4M3 block scales of this member, dense,
+ *                 rewritten in place; any alignment
+ *   tensor_scale: one fp32 s_t of this member (finite, >= 0), read, then
+ *                 overwritten with the shared scale
+ */
+typedef struct fp4q_nv_member {
+  uint8_t* scales;
+  float* tensor_scale;
+  int64_t rows;
+  int64_t cols;
+} fp4q_nv_member;
+
+/*
+ * Shared tensor scale for the members of a fused NVFP4 GEMM.  [GDN]
+ * background box on fused GEMMs and the global-scale mismatch, and step (2)
+ * of its pipeline: the fused GEMM applies ONE tensor scale, the largest
+ * member scale; each member's ratio is folded into its E4M3 block scales
+ * (codes unchanged), which re-rounds each block scale by at most half an
+ * E4M3 step (1/16 relative for normal results).  Binary32, per member i:
+ *   s_t = max_i s_t,i;  r_i = s_t,i / s_t (1 when s_t == 0);
+ *   s_b' = E4M3 value nearest to fl(s_b * r_i), ties to the even byte.
+ * Bytes with the sign bit set or NaN (0x7F, 0xFF) are left unchanged.
+ * Afterwards every members[i].tensor_scale and *shared_tensor_scale hold s_t
+ * (shared_tensor_scale may be one of the member cells), so a second call is
+ * the identity.  Two kernels on `stream`; nothing is allocated.
+ * n_members in [1, 16]; every member: rows >= 1, cols a multiple of 16; the
+ * members' scale ranges must not overlap each other or any scale cell
+ * (FP4Q_ERR_BAD_ARG).
+ */
+int fp4q_harmonize_nvfp4(const fp4q_nv_member* members, int n_members,
+                         float* shared_tensor_scale, void* stream);
+
+/*
  * W4A4 GEMM over quantized operands: Y = dequant(A) * dequant(B)^T, fp32
  * accumulate, fp32 out.  [MQ] "Core method" (y = [(x*t)B]_MXFP4 W'^T_MXFP4)
  * and [GDN] "NVFP4 and W4A4" (both operands NVFP4, GEMM on the 4-bit data).

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_hadamard32_scale",
               "fp4q_sigma_delta_requant", "fp4q_gemm_w4a4", "fp4q_gemm_w4a16", "fp4q_linear_w4a4",
-              "fp4q_balance_scale", "fp4q_abi_version", "fp4q_status_str", "fp4q_last_error"]:
+              "fp4q_balance_scale", "fp4q_harmonize_nvfp4", "fp4q_abi_version", "fp4q_status_str",
+              "fp4q_last_error"]:
         assert n in names
 
 
@@ -85,6 +86,27 @@ def test_validation_happens_before_any_device_work(fp4q):
         assert L.fp4q_linear_w4a4(fake16, 128, fake, 0, fake16, fake16, fake, m, n, k, fake16, 8, None) == 2
     seg0 = fp4q.SdSegment(0x10000, 0x1000, 0x1000, 0x10000, 0x10000, 0, 32)
     assert L.fp4q_sigma_delta_requant((fp4q.SdSegment * 1)(seg0), 1, 1, 0, None) == 2
+
+
+def test_harmonize_validation(fp4q):
+    L, M = fp4q.lib, fp4q.NvMember
+    cell = ctypes.c_void_p(0x90000)
+
+    def call(*mems, shared=cell):
+        return L.fp4q_harmonize_nvfp4((M * max(len(mems), 1))(*mems), len(mems), shared, None)
+
+    a = M(0x10000, 0x80000, 8, 64)                   # 32 scale bytes at 0x10000
+    b = M(0x20000, 0x80004, 8, 64)
+    assert call(a, b, shared=None) == 1
+    assert call(M(0, 0x80000, 8, 64), b) == 1
+    assert call() == 5                                          # n_members = 0
+    assert L.fp4q_harmonize_nvfp4((M * 17)(*([a] * 17)), 17, cell, None) == 5
+    assert call(M(0x10000, 0x80000, 8, 40), b) == 2             # cols % 16
+    assert call(M(0x10000, 0x80000, 0, 64), b) == 2             # empty
+    assert call(a, M(0x1001F, 0x80004, 8, 64)) == 5             # scale ranges overlap by one byte
+    assert call(a, M(0x20000, 0x1001C, 8, 64)) == 5             # a tensor-scale cell inside a's scales
+    assert call(a, b, shared=ctypes.c_void_p(0x2001D)) == 5     # shared cell straddles b's last bytes
+    assert b"overlap" in L.fp4q_last_error()
 
 
 def test_device_check_without_gpu(fp4q):
