@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 WARM_S = 0.3          # minimum seconds of untimed warm-up before any timed region
 PEAK = {"hbm_GBps": 8000.0, "fp4_TFLOPs": 10100.0, "fp8_TFLOPs": 5000.0, "fp16_TFLOPs": 2500.0,
-        "bf16_TFLOPs": 2500.0}
+        "bf16_TFLOPs": 2500.0, "fp64_TFLOPs": 78.6}
 
 
 def parse():
@@ -264,6 +264,38 @@ def run_extras(L, synth, np, torch, dev, stream, log):
     mx["online_step_quantize_x_plus_gemm"] = _fl(st, 2.0 * M * N * K, "fp4_TFLOPs")
     ex["mxfp4_transform_2048x14336x4096"] = mx
     del xs, ws, xc, wc, y, x, w
+    torch.cuda.empty_cache()
+
+    # ---------------- MACaQ weight-side refinement of the MXFP4 layer's weight
+    # (14336 x 4096) on its 2048 calibration rows, both transformed
+    log("extras: MACaQ Hessian + exponent screen + Flip-Refinement")
+    wl = synth.mxfp4_transform()
+    M, N, K = wl.meta["M"], wl.meta["N"], wl.meta["K"]
+    x, w = bf16(wl.arrays["x_bf16"]), bf16(wl.arrays["w_bf16"])
+    del wl
+    t, u = L.balance_scale(w, x)
+    xp, wp = L.hadamard32_scale(x, t), L.hadamard32_scale(w, u)
+    del x, w
+    h = torch.zeros((K, K), dtype=torch.float64, device=dev)
+    hz = _time_op(torch, stream, lambda i: L.hessian_accumulate(xp, h), 10)
+    h.zero_()
+    L.hessian_accumulate(xp, h)
+    ws = torch.empty(L.lib.fp4q_macaq_workspace_bytes(N, K) // 8, dtype=torch.float64, device=dev)
+    res = {}
+
+    def refine(i, k):
+        res[k] = L.macaq_refine(wp, h, 1.0, k, workspace=ws)
+
+    mq = {"weight": [N, K], "calibration_rows": M, "lambda": 1.0}
+    mq["hessian_accumulate"] = _fl(hz, 2.0 * K * K * M, "fp64_TFLOPs")
+    mq["screen_only_K0"] = {k: round(v, 4) for k, v in _time_op(torch, stream, lambda i: refine(i, 0), 5).items()}
+    mq["refine_K128"] = {k: round(v, 4) for k, v in _time_op(torch, stream, lambda i: refine(i, 128), 5).items()}
+    fl = res[128][2].to(torch.int64)
+    mq["flips_per_row_mean"] = round(float(fl.float().mean()), 2)
+    mq["rows_at_K"] = int((fl == 128).sum())
+    mq["gradient_flops"] = 2.0 * N * K * K
+    ex["macaq_refine_14336x4096"] = mq
+    del xp, wp, h, ws, res
     torch.cuda.empty_cache()
 
     # ---------------- NVFP4 4/6 block scales on the prefill weight (10240 x 5120)

@@ -229,6 +229,41 @@ int fp4q_harmonize_nvfp4(const fp4q_nv_member* members, int n_members,
                        "harmonize_nvfp4");
 }
 
+int fp4q_hessian_accumulate(const float* x, int64_t T, int64_t n, int64_t ldx, double* h, void* stream) {
+  g_last_error[0] = 0;
+  if (!x || !h) return fail(FP4Q_ERR_NULL_PTR, "x or h is NULL");
+  if (T < 1 || n < 1 || n > 65536 || ldx < n) return fail(FP4Q_ERR_BAD_SHAPE, "bad shape (T >= 1, 1 <= n <= 65536, ldx >= n)");
+  if (T > (int64_t(1) << 40) / ldx) return fail(FP4Q_ERR_BAD_SHAPE, "x too large");
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_hessian(x, T, n, ldx, h, as_stream(stream)), "hessian_accumulate");
+}
+
+int64_t fp4q_macaq_workspace_bytes(int64_t m, int64_t n) {
+  if (m < 1 || n < 1 || n > 16384 || m > (int64_t(1) << 40) / n) return -1;
+  return 8 * (32 + ((n + 31) / 32) * 32 + m * n);
+}
+
+int fp4q_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lambda,
+                      int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!w || !h || !codes || !scales || !workspace)
+    return fail(FP4Q_ERR_NULL_PTR, "w, h, codes, scales and workspace are required");
+  if (m < 1 || n < 32 || n % 32 || n > 16384 || ldw < n || ldw % 4)
+    return fail(FP4Q_ERR_BAD_SHAPE, "bad shape (m >= 1, n % 32 == 0, 32 <= n <= 16384, ldw >= n, ldw % 4 == 0)");
+  if (m > (int64_t(1) << 40) / ldw) return fail(FP4Q_ERR_BAD_SHAPE, "w too large");
+  if (!aligned16(w) || !aligned16(codes)) return fail(FP4Q_ERR_BAD_ALIGN, "w and codes must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(FP4Q_ERR_BAD_ALIGN, "workspace must be 8-byte aligned");
+  if (!(lambda >= 0.0) || lambda > 1e300) return fail(FP4Q_ERR_BAD_ARG, "lambda must be finite and >= 0");
+  if (k_iters < 0 || k_iters > (1 << 20)) return fail(FP4Q_ERR_BAD_ARG, "k_iters must be in [0, 2^20]");
+  if (workspace_bytes < fp4q_macaq_workspace_bytes(m, n))
+    return fail(FP4Q_ERR_BAD_ARG, "workspace too small (%lld bytes needed)", (long long)fp4q_macaq_workspace_bytes(m, n));
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_macaq_refine(w, m, n, ldw, h, lambda, k_iters, codes, scales, flips,
+                                                 static_cast<double*>(workspace), as_stream(stream)),
+                       "macaq_refine");
+}
+
 int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
                    int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream) {

@@ -36,6 +36,10 @@ hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K,
 hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
                               int64_t bank_stride, hipStream_t s);
 hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* shared, hipStream_t s);
+hipError_t launch_hessian(const float* x, int64_t T, int64_t n, int64_t ldx, double* h, hipStream_t s);
+hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lam,
+                               int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, double* ws,
+                               hipStream_t s);
 
 hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,

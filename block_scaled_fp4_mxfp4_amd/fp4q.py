@@ -51,6 +51,9 @@ _SIGS = {
     "fp4q_balance_scale": ([_p, _i, _l, _l, _l, _p, _i, _l, _l, ctypes.c_double, _p, _p, _p], _i),
     "fp4q_sigma_delta_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, _p], _i),
     "fp4q_harmonize_nvfp4": ([ctypes.POINTER(NvMember), _i, _p, _p], _i),
+    "fp4q_hessian_accumulate": ([_p, _l, _l, _l, _p, _p], _i),
+    "fp4q_macaq_workspace_bytes": ([_l, _l], _l),
+    "fp4q_macaq_refine": ([_p, _l, _l, _l, _p, ctypes.c_double, _i, _p, _p, _p, _p, _l, _p], _i),
     "fp4q_gemm_w4a4": ([_i, _p, _p, _p, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_gemm_w4a16": ([_p, _l, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_linear_w4a4": ([_p, _l, _p, _i, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
@@ -205,6 +208,41 @@ def harmonize_nvfp4(scales: Sequence[torch.Tensor], tensor_scales: Sequence[torc
     out = torch.empty(1, dtype=torch.float32, device=dev) if shared is None else shared
     _check(lib.fp4q_harmonize_nvfp4(arr, len(scales), _ptr(out), _stream(dev)), "harmonize_nvfp4")
     return out
+
+
+def hessian_accumulate(x: torch.Tensor, h: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h += x^T x (float64 [n, n]) for fp32 calibration rows x [T, n];
+    a zero h is allocated when none is given."""
+    if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be fp32 [T, n] with unit column stride")
+    n = x.shape[1]
+    if h is None:
+        h = torch.zeros((n, n), dtype=torch.float64, device=x.device)
+    _check(lib.fp4q_hessian_accumulate(_ptr(x), x.shape[0], n, x.stride(0), _ptr(h), _stream(x.device)),
+           "hessian_accumulate")
+    return h
+
+
+def macaq_refine(w: torch.Tensor, h: torch.Tensor, lam: float = 1.0, k_iters: int = 128,
+                 workspace: Optional[torch.Tensor] = None):
+    """Exponent screen + Flip-Refinement of the fp32 transformed weight w
+    [m, n] under the calibration Hessian h [n, n] (float64).  Returns
+    (codes uint8 [m, n/2], scales uint8 [m, n/32], flips int32 [m])."""
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be fp32 [m, n] with unit column stride")
+    if h.dtype != torch.float64 or not h.is_contiguous():
+        raise ValueError("h must be contiguous float64 [n, n]")
+    m, n = w.shape
+    codes = torch.empty((m, n // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((m, n // 32), dtype=torch.uint8, device=w.device)
+    flips = torch.empty(m, dtype=torch.int32, device=w.device)
+    need = lib.fp4q_macaq_workspace_bytes(m, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8) // 8, dtype=torch.float64, device=w.device)
+    _check(lib.fp4q_macaq_refine(_ptr(w), m, n, w.stride(0), _ptr(h), float(lam), int(k_iters), _ptr(codes),
+                                 _ptr(scales), _ptr(flips), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(w.device)), "macaq_refine")
+    return codes, scales, flips
 
 
 # ----------------------------------------------------------------- GEMM ----

@@ -238,6 +238,57 @@ int fp4q_harmonize_nvfp4(const fp4q_nv_member* members, int n_members,
                          float* shared_tensor_scale, void* stream);
 
 /*
+ * Calibration Hessian for the MXFP4 weight refinement.  [MQ] "Method steps"
+ * 0 (H = sum over calibration chunks of X^T X, accumulated chunk by chunk)
+ * and "Core method" (iii)-(iv) (H taken in the domain of the transformed
+ * weight: pass X' = (X * t) B, e.g. from fp4q_hadamard32_scale).
+ *   x: [T][ldx] fp32 calibration rows (device), ldx >= n
+ *   h: [n][n] fp64 (device), read and written: h_jk += sum_t x_tj * x_tk,
+ *      float64, tokens in order (products of two floats are exact), so
+ *      chunks passed in order equal one call on their concatenation.  The
+ *      caller zeroes h before the first chunk.
+ * T >= 1, 1 <= n <= 65536.
+ */
+int fp4q_hessian_accumulate(const float* x, int64_t T, int64_t n, int64_t ldx, double* h, void* stream);
+
+/*
+ * Bytes of device workspace fp4q_macaq_refine needs for an m x n weight:
+ * 8 * (32 + n + m * n).
+ */
+int64_t fp4q_macaq_workspace_bytes(int64_t m, int64_t n);
+
+/*
+ * MACaQ weight-side refinement of an MXFP4 weight.  [MQ] "Core method"
+ * (iii) and (iv), "Method steps" 3 and 4 (equation 12, Algorithm 1):
+ *   H_f = H + lambda * mean(diag H) * I;
+ *   per row and 32-block, among the standard exponent e0 (block maximum, as
+ *   fp4q_quantize_mxfp4 takes it), e0 + 1 and e0 - 1 keep the one with the
+ *   least sum_j (H_f)_jj (w_j - What_j(e))^2 (What: nearest codes at 2^e);
+ *   then up to k_iters rounds of Flip-Refinement per row: the move of one
+ *   code to an adjacent E2M1 value with the largest positive
+ *   gain = 2 D g_ij - D^2 (H_f)_jj is taken and g_i -= D (H_f)_j, with
+ *   g_i = (w_i - What_i) H_f; a row stops when no gain is positive.
+ * float64, every sum in a fixed sequential order; ties keep e0 (then try
+ * e0 + 1 before e0 - 1) and take the smallest j, the move down first.  A
+ * zero value is code 0x8 when w is negative (sign bit); an all-zero block
+ * keeps scale byte 0 and codes 0.
+ *   w:         [m][ldw] fp32 transformed weight W' (device, 16-byte aligned,
+ *              ldw >= n, ldw % 4 == 0)
+ *   h:         [n][n] fp64 calibration Hessian (symmetric), not modified
+ *   lambda:    ridge factor (finite, >= 0; the page uses 1.0)
+ *   k_iters:   maximum flips per row (the page uses 128); 0 = screen only
+ *   codes:     [m][n/2] packed E2M1 codes (output, 16-byte aligned)
+ *   scales:    [m][n/32] E8M0 bytes (output)
+ *   flips:     [m] int32 flips taken per row (output) or NULL
+ *   workspace: >= fp4q_macaq_workspace_bytes(m, n) bytes of device memory,
+ *              8-byte aligned, contents destroyed
+ * n % 32 == 0, 32 <= n <= 16384, m >= 1.  Four kernels on `stream`.
+ */
+int fp4q_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lambda,
+                      int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+
+/*
  * W4A4 GEMM over quantized operands: Y = dequant(A) * dequant(B)^T, fp32
  * accumulate, fp32 out.  [MQ] "Core method" (y = [(x*t)B]_MXFP4 W'^T_MXFP4)
  * and [GDN] "NVFP4 and W4A4" (both operands NVFP4, GEMM on the 4-bit data).

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_hadamard32_scale",
               "fp4q_sigma_delta_requant", "fp4q_gemm_w4a4", "fp4q_gemm_w4a16", "fp4q_linear_w4a4",
-              "fp4q_balance_scale", "fp4q_harmonize_nvfp4", "fp4q_abi_version", "fp4q_status_str",
+              "fp4q_balance_scale", "fp4q_harmonize_nvfp4", "fp4q_hessian_accumulate",
+              "fp4q_macaq_workspace_bytes", "fp4q_macaq_refine", "fp4q_abi_version", "fp4q_status_str",
               "fp4q_last_error"]:
         assert n in names
 
@@ -116,3 +117,30 @@ def test_device_check_without_gpu(fp4q):
     fake16 = ctypes.c_void_p(0x10000)
     st = fp4q.lib.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, fake16, fake16, 0, None)
     assert st == 6
+
+
+def test_macaq_validation(fp4q):
+    L = fp4q.lib
+    P = ctypes.c_void_p
+    f16, f8 = P(0x10000), P(0x10008)
+    assert L.fp4q_hessian_accumulate(None, 4, 8, 8, f16, None) == 1
+    assert L.fp4q_hessian_accumulate(f16, 0, 8, 8, f16, None) == 2
+    assert L.fp4q_hessian_accumulate(f16, 4, 8, 4, f16, None) == 2           # ldx < n
+    assert L.fp4q_macaq_workspace_bytes(10, 64) == 8 * (32 + 64 + 640)
+    assert L.fp4q_macaq_workspace_bytes(10, 16400) == -1
+    ws = L.fp4q_macaq_workspace_bytes(10, 64)
+    ok = dict(w=f16, m=10, n=64, ldw=64, h=f16, lam=1.0, k=128, codes=f16, scales=f16, flips=None,
+              ws=f16, wsb=ws)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.fp4q_macaq_refine(a["w"], a["m"], a["n"], a["ldw"], a["h"], a["lam"], a["k"], a["codes"],
+                                   a["scales"], a["flips"], a["ws"], a["wsb"], None)
+
+    assert call(h=None) == 1
+    assert call(n=48) == 2 and call(n=16) == 2 and call(n=16416, ldw=16416) == 2
+    assert call(ldw=66) == 2 and call(m=0) == 2
+    assert call(w=P(0x10004)) == 3 and call(codes=f8) == 3 and call(ws=P(0x10004)) == 3
+    assert call(lam=-1.0) == 5 and call(lam=float("nan")) == 5 and call(k=-1) == 5
+    assert call(wsb=ws - 8) == 5
+    assert b"workspace" in L.fp4q_last_error()
