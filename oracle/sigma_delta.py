@@ -119,3 +119,16 @@ def sigma_delta_nvfp4(w: np.ndarray, steps: int, r0: np.ndarray = None, tensor_s
         codes_all.append(codes)
         res_all.append(r.copy())
     return {"codes": codes_all, "residues": res_all, "scales": sb_bytes, "s_t": s_t}
+
+
+def reverse_tail_schedule(w: np.ndarray, n_rtn: int, n_tail: int, tensor_scale=None, rule: str = "6"):
+    """Code banks for n_rtn + n_tail accesses with the reverse-order tail
+    (loopquant page, section 2.3): the first ``n_rtn`` accesses use the
+    plain nearest code; the last ``n_tail`` run a fresh chain from r_0 = 0
+    and take its codes in reverse, tail access j using the chain's code
+    n_tail - j + 1, so the last access gets the chain's first code (the
+    nearest code) and the chain's final residue r_K meets the tail's first
+    access.  Returns the list of banks (uint8 [R, K] unpacked), access
+    order."""
+    chain = sigma_delta_nvfp4(w, n_tail, tensor_scale=tensor_scale, rule=rule)["codes"]
+    return [chain[0].copy() for _ in range(n_rtn)] + [c.copy() for c in chain[::-1]]

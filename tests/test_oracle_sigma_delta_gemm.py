@@ -164,3 +164,31 @@ def test_sigma_delta_on_46_scales_keeps_the_residue_bound():
     x, _, _, _ = SD.normalised_weight(w, rule="4/6")
     mean_q = np.mean([F.e2m1_decode(c) for c in ref["codes"]], axis=0)
     assert np.abs(mean_q - x).max() <= 1.0 / 32 + 1e-6
+
+
+def test_reverse_tail_schedule():
+    # loopquant page, section 2.3: B plain nearest-code accesses, then a fresh
+    # chain of K codes used in reverse; the last access takes the nearest
+    # code and the tail's total error is the chain's -r_K, now met at the
+    # tail's first access
+    w = synth.normal_f32(44, (24, 128), 0.02)
+    w[2, :16] = 0.0
+    B, K = 3, 6
+    banks = SD.reverse_tail_schedule(w, B, K)
+    assert len(banks) == B + K
+    codes_rtn, _, _ = nvfp4.quantize(w)
+    for b in banks[:B]:
+        assert np.array_equal(b, codes_rtn)
+    assert np.array_equal(banks[-1], codes_rtn)              # last access: the chain's first code
+    chain = SD.sigma_delta_nvfp4(w, K)
+    assert np.array_equal(banks[B], chain["codes"][K - 1])   # tail entrance: the chain's last code
+    x, _, _, _ = SD.normalised_weight(w)
+    x = x.astype(np.float64)
+    tail_err = sum(F.e2m1_decode(c) - x for c in banks[B:])
+    assert np.abs(tail_err + chain["residues"][K - 1].astype(np.float64)).max() <= K * 2.0 ** -21
+    # K = 1: every access is the nearest code
+    assert all(np.array_equal(b, codes_rtn) for b in SD.reverse_tail_schedule(w, 2, 1))
+    # the worked example of section 2.1 reversed: x = 0.3 on the integer grid
+    q_int = lambda v: Fraction(math.floor(v + Fraction(1, 2)))
+    qs, _ = SD.sigma_delta_exact(Fraction(3, 10), q_int, 8)
+    assert [int(q) for q in qs[::-1]] == [0, 0, 0, 1, 0, 0, 1, 0]
