@@ -413,6 +413,22 @@ def run_extras(L, synth, np, torch, dev, stream, log):
     tfw = _time_op(torch, stream, full_forward, 3, warm=1)
     sd["forward_R32_ms"] = round(tfw["median_ms"], 3)
     sd["forward_R32_per_step_ms"] = round(tfw["median_ms"] / R, 4)
+
+    # all R code banks in one launch: the plain multi-bank chain and the
+    # reverse-order tail schedule (R/2 nearest-code banks + R/2 tail codes)
+    stride = -(-max(s_["w"].numel() // 2 for s_ in segs) // 16) * 16
+    banks = [torch.empty((R, stride), dtype=torch.uint8, device=dev) for _ in segs]
+    msegs = [{**s_, "codes": b} for s_, b in zip(segs, banks)]
+
+    def multibank(_):
+        L.sigma_delta_requant(msegs, steps=R, bank_stride=stride)
+
+    def schedule(_):
+        L.sigma_delta_schedule(msegs, R // 2, R - R // 2, bank_stride=stride)
+
+    sd["multibank_R32_one_launch"] = _bw(_time_op(torch, stream, multibank, 10), nw * (4 + 4 + 4 + 0.5 * R + 1 / 16))
+    sd["reverse_tail_16_plus_16_one_launch"] = _bw(_time_op(torch, stream, schedule, 10), nw * (4 + 0.5 * R + 1 / 16))
+    del banks, msegs
     ex["looped_sigma_delta_13x_R32"] = sd
     del segs, gem
     torch.cuda.empty_cache()

@@ -191,9 +191,34 @@ int fp4q_sigma_delta_requant(const fp4q_sd_segment* segs, int nseg, int steps,
       return fail(FP4Q_ERR_BAD_ARG, "segment %d: bank_stride_bytes too small or not a multiple of 16", i);
   }
   if (int st = check_device()) return st;
-  return launch_status(fp4q::launch_sigma_delta(segs, nseg, steps, steps > 1 ? bank_stride_bytes : 0,
+  return launch_status(fp4q::launch_sigma_delta(segs, nseg, steps, steps > 1 ? bank_stride_bytes : 0, 0, 0,
                                                 as_stream(stream)),
                        "sigma_delta_requant");
+}
+
+int fp4q_sigma_delta_schedule(const fp4q_sd_segment* segs, int nseg, int n_rtn, int n_tail,
+                              int64_t bank_stride_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!segs) return fail(FP4Q_ERR_NULL_PTR, "segs is NULL");
+  if (nseg < 1 || nseg > 64) return fail(FP4Q_ERR_BAD_ARG, "nseg must be in [1, 64]");
+  if (n_rtn < 0 || n_tail < 1 || n_rtn > 4096 || n_tail > 4096)
+    return fail(FP4Q_ERR_BAD_ARG, "n_rtn must be in [0, 4096] and n_tail in [1, 4096]");
+  const int banks = n_rtn + n_tail;
+  for (int i = 0; i < nseg; ++i) {
+    const fp4q_sd_segment& g = segs[i];
+    if (!g.w || !g.scales || !g.tensor_scale || !g.codes)
+      return fail(FP4Q_ERR_NULL_PTR, "segment %d has a NULL pointer", i);
+    if (g.rows <= 0 || g.cols <= 0 || g.cols % 16) return fail(FP4Q_ERR_BAD_SHAPE, "segment %d: bad shape", i);
+    if (g.rows * g.cols > (int64_t(1) << 34)) return fail(FP4Q_ERR_BAD_SHAPE, "segment %d: too large", i);
+    if (!aligned16(g.w) || !aligned16(g.codes))
+      return fail(FP4Q_ERR_BAD_ALIGN, "segment %d: w and codes must be 16-byte aligned", i);
+    if (banks > 1 && (bank_stride_bytes < g.rows * g.cols / 2 || bank_stride_bytes % 16))
+      return fail(FP4Q_ERR_BAD_ARG, "segment %d: bank_stride_bytes too small or not a multiple of 16", i);
+  }
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_sigma_delta(segs, nseg, n_tail, banks > 1 ? bank_stride_bytes : 0, 1, n_rtn,
+                                                as_stream(stream)),
+                       "sigma_delta_schedule");
 }
 
 int fp4q_harmonize_nvfp4(const fp4q_nv_member* members, int n_members,

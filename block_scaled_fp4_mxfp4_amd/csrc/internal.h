@@ -33,8 +33,10 @@ hipError_t launch_hadamard32_scale(const void* x, int bf16, int64_t rows, int64_
 hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K, int64_t ldw,
                                 const void* x, int x_bf16, int64_t M, int64_t ldx, double alpha,
                                 float* t_out, float* u_out, hipStream_t s);
+// sched != 0: the reverse-order tail schedule (n_rtn nearest-code banks,
+// then `steps` chain codes in reverse; no residue buffer)
 hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
-                              int64_t bank_stride, hipStream_t s);
+                              int64_t bank_stride, int sched, int n_rtn, hipStream_t s);
 hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* shared, hipStream_t s);
 hipError_t launch_hessian(const float* x, int64_t T, int64_t n, int64_t ldx, double* h, hipStream_t s);
 hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lam,

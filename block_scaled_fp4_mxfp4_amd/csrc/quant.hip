@@ -441,8 +441,13 @@ struct SdArgs {
 #endif
 constexpr int kSdUnroll = FP4Q_SD_UNROLL;
 
+// SCHED: the reverse-order tail schedule -- the chain starts from r = 0 on
+// chip (no residue buffer), runs `steps` = K steps, writes step k (0-based)
+// to bank n_rtn + K - 1 - k and, at k = 0, the same codes (the nearest
+// codes) to banks 0 .. n_rtn - 1.
+template <bool SCHED>
 __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int steps,
-                                                          int64_t bank_stride) {
+                                                          int64_t bank_stride, int n_rtn) {
   int seg = 0;
   while (seg + 1 < args.nseg && (int)blockIdx.x >= args.wg_start[seg + 1]) ++seg;
   const int64_t wg = (int64_t)blockIdx.x - args.wg_start[seg];
@@ -458,7 +463,12 @@ __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int
     cidx[u] = (wg * kSdUnroll + u) * kThreads + threadIdx.x;
     const int64_t cl = clamp_chunk(cidx[u], n);
     load8<false>(w, cl * 8, x[u]);
-    load8<false>(res, cl * 8, r[u]);
+    if (SCHED) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[u][i] = 0.0f;
+    } else {
+      load8<false>(res, cl * 8, r[u]);
+    }
     sb_raw[u] = args.scales[seg][cl >> 1];
   }
 #pragma unroll
@@ -502,10 +512,15 @@ __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int
         r[u][2 * i] = v0 - q0;
         r[u][2 * i + 1] = v1 - q1;
       }
-      if (cidx[u] < n)
-        reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pk;
+      if (cidx[u] < n) {
+        const int64_t bank = SCHED ? (int64_t)(n_rtn + steps - 1 - k) : (int64_t)k;
+        reinterpret_cast<uint32_t*>(codes + bank * bank_stride)[cidx[u]] = pk;
+        if (SCHED && k == 0)
+          for (int b = 0; b < n_rtn; ++b) reinterpret_cast<uint32_t*>(codes + (int64_t)b * bank_stride)[cidx[u]] = pk;
+      }
     }
   }
+  if (SCHED) return;
 #pragma unroll
   for (int u = 0; u < kSdUnroll; ++u) {
     if (cidx[u] < n) {
@@ -728,7 +743,7 @@ hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K,
 }
 
 hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
-                              int64_t bank_stride, hipStream_t s) {
+                              int64_t bank_stride, int sched, int n_rtn, hipStream_t s) {
   for (int base = 0; base < nseg; base += kSdMaxSeg) {
     SdArgs a = {};
     const int cnt = (nseg - base) < kSdMaxSeg ? (nseg - base) : kSdMaxSeg;
@@ -746,7 +761,8 @@ hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
       wg += (int32_t)grid_for(a.nchunks[i], (int64_t)kThreads * kSdUnroll);
     }
     a.wg_start[cnt] = wg;
-    hipLaunchKernelGGL(k_sigma_delta, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride);
+    if (sched) hipLaunchKernelGGL(k_sigma_delta<true>, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride, n_rtn);
+    else hipLaunchKernelGGL(k_sigma_delta<false>, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -50,6 +50,7 @@ _SIGS = {
     "fp4q_hadamard32_scale": ([_p, _i, _l, _l, _l, _p, _p, _l, _p], _i),
     "fp4q_balance_scale": ([_p, _i, _l, _l, _l, _p, _i, _l, _l, ctypes.c_double, _p, _p, _p], _i),
     "fp4q_sigma_delta_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, _p], _i),
+    "fp4q_sigma_delta_schedule": ([ctypes.POINTER(SdSegment), _i, _i, _i, _l, _p], _i),
     "fp4q_harmonize_nvfp4": ([ctypes.POINTER(NvMember), _i, _p, _p], _i),
     "fp4q_hessian_accumulate": ([_p, _l, _l, _l, _p, _p], _i),
     "fp4q_macaq_workspace_bytes": ([_l, _l], _l),
@@ -243,6 +244,23 @@ def macaq_refine(w: torch.Tensor, h: torch.Tensor, lam: float = 1.0, k_iters: in
                                  _ptr(scales), _ptr(flips), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(w.device)), "macaq_refine")
     return codes, scales, flips
+
+
+def sigma_delta_schedule(segments: Sequence[dict], n_rtn: int, n_tail: int, bank_stride: int = 0) -> None:
+    """Write n_rtn + n_tail code banks per weight with the reverse-order
+    tail (n_rtn nearest-code banks, then a fresh chain of n_tail codes in
+    reverse).  Segments as for :func:`sigma_delta_requant`; ``residue`` is
+    not used."""
+    arr = (SdSegment * len(segments))()
+    dev = None
+    for i, s in enumerate(segments):
+        w = s["w"]
+        dev = w.device
+        res = s.get("residue")
+        arr[i] = SdSegment(w.data_ptr(), s["scales"].data_ptr(), s["tensor_scale"].data_ptr(),
+                           0 if res is None else res.data_ptr(), s["codes"].data_ptr(), w.shape[0], w.shape[1])
+    _check(lib.fp4q_sigma_delta_schedule(arr, len(segments), int(n_rtn), int(n_tail), int(bank_stride),
+                                         _stream(dev)), "sigma_delta_schedule")
 
 
 # ----------------------------------------------------------------- GEMM ----

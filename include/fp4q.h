@@ -202,6 +202,22 @@ int fp4q_sigma_delta_requant(const fp4q_sd_segment* segs, int nseg, int steps,
                              int64_t bank_stride_bytes, void* stream);
 
 /*
+ * Code banks for n_rtn + n_tail loop accesses with the reverse-order tail.
+ * [LQ] section 2.3 (partial summation and the reverse-order tail): the
+ * first n_rtn accesses use the plain nearest code; the last n_tail run a
+ * fresh chain from r_0 = 0 and use its codes in reverse, tail access j
+ * taking the chain's code n_tail - j + 1, so the last access gets the
+ * nearest code and the chain's final residue meets the tail's first
+ * access.  Same per-element arithmetic as fp4q_sigma_delta_requant; one
+ * launch; the residue field of the segments is not used (may be NULL).
+ * Access b (0-based) is written at segs[i].codes + b * bank_stride_bytes
+ * (ignored when n_rtn + n_tail == 1, else >= rows*cols/2 and a multiple of
+ * 16).  n_rtn in [0, 4096], n_tail in [1, 4096], nseg in [1, 64].
+ */
+int fp4q_sigma_delta_schedule(const fp4q_sd_segment* segs, int nseg, int n_rtn, int n_tail,
+                              int64_t bank_stride_bytes, void* stream);
+
+/*
  * One member of a fused NVFP4 GEMM (weights quantized separately and
  * concatenated along N).  The ARRAY of members lives in HOST memory; the
  * pointers inside it are device pointers.

@@ -87,7 +87,8 @@ def normalised_weight(w: np.ndarray, tensor_scale=None, rule: str = "6"):
     s = (s_t * s_b).astype(F32)
     with np.errstate(divide="ignore"):
         rho = (F32(1.0) / s).astype(F32)
-    x = (w * np.repeat(rho, nvfp4.BLOCK, axis=1)).astype(F32)
+    with np.errstate(invalid="ignore"):                      # 0 * inf in zero blocks, replaced below
+        x = (w * np.repeat(rho, nvfp4.BLOCK, axis=1)).astype(F32)
     zero = np.repeat(s == 0, nvfp4.BLOCK, axis=1)
     x = np.where(zero, F32(0), x)
     x = np.clip(x, F32(-6.0), F32(6.0)).astype(F32)

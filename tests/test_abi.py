@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for n in ["fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_hadamard32_scale",
               "fp4q_sigma_delta_requant", "fp4q_gemm_w4a4", "fp4q_gemm_w4a16", "fp4q_linear_w4a4",
               "fp4q_balance_scale", "fp4q_harmonize_nvfp4", "fp4q_hessian_accumulate",
-              "fp4q_macaq_workspace_bytes", "fp4q_macaq_refine", "fp4q_abi_version", "fp4q_status_str",
+              "fp4q_macaq_workspace_bytes", "fp4q_macaq_refine", "fp4q_sigma_delta_schedule",
+              "fp4q_abi_version", "fp4q_status_str",
               "fp4q_last_error"]:
         assert n in names
 
@@ -87,6 +88,13 @@ def test_validation_happens_before_any_device_work(fp4q):
         assert L.fp4q_linear_w4a4(fake16, 128, fake, 0, fake16, fake16, fake, m, n, k, fake16, 8, None) == 2
     seg0 = fp4q.SdSegment(0x10000, 0x1000, 0x1000, 0x10000, 0x10000, 0, 32)
     assert L.fp4q_sigma_delta_requant((fp4q.SdSegment * 1)(seg0), 1, 1, 0, None) == 2
+    # the reverse-tail schedule: residue not required; bank counts and stride checked
+    segn = (fp4q.SdSegment * 1)(fp4q.SdSegment(0x10000, 0x1000, 0x1000, 0, 0x10000, 4, 32))
+    assert L.fp4q_sigma_delta_schedule(segn, 1, -1, 4, 64, None) == 5
+    assert L.fp4q_sigma_delta_schedule(segn, 1, 2, 0, 64, None) == 5
+    assert L.fp4q_sigma_delta_schedule(segn, 1, 2, 4, 32, None) == 5                  # stride < 64
+    assert L.fp4q_sigma_delta_schedule(segn, 0, 2, 4, 64, None) == 5
+    assert L.fp4q_sigma_delta_schedule((fp4q.SdSegment * 1)(seg0), 1, 2, 4, 64, None) == 2
 
 
 def test_harmonize_validation(fp4q):

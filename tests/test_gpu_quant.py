@@ -369,7 +369,8 @@ def test_sigma_delta_looped_core_full_size_sampled_rows():
     samples = [sample_rows(w.shape[0], k=12, seed=i) for i, w in enumerate(ws)]
     refs = []
     for w, rows, s in zip(ws, samples, segs):
-        st = host(s["tensor_scale"])[0]
+        st = ONV.tensor_scale_from_amax(np.abs(w).max())      # the oracle's own, over the whole weight
+        assert host(s["tensor_scale"])[0] == st
         refs.append(OSD.sigma_delta_nvfp4(w[rows], 32, tensor_scale=st))
     for k in range(32):
         L.sigma_delta_requant(segs, steps=1)
@@ -377,3 +378,46 @@ def test_sigma_delta_looped_core_full_size_sampled_rows():
             for s, ref, rows in zip(segs, refs, samples):
                 assert_bytes_equal(host(s["codes"][0])[rows], packed(ref["codes"][k]), f"step {k}")
                 assert_bytes_equal(host(s["residue"])[rows].view(np.uint32), ref["residues"][k].view(np.uint32), f"res {k}")
+
+
+def test_sigma_delta_reverse_tail_schedule():
+    # B nearest-code banks, then a fresh chain of K codes in reverse, one launch
+    ws = [synth.normal_f32(130 + i, shp, 0.02) for i, shp in enumerate([(48, 64), (16, 128), (7, 32)])]
+    ws[0][5, 16:32] = 0.0
+    L = fp4q()
+    for B, K in ((3, 5), (0, 4), (2, 1), (0, 1)):
+        segs, _ = _sd_segments(ws)
+        stride = -(-max(w.size // 2 for w in ws) // 16) * 16
+        for s_ in segs:
+            s_["codes"] = torch.empty((B + K, stride), dtype=torch.uint8, device=s_["w"].device)
+            s_["residue"] = None
+        print(f"reverse-tail schedule B={B} K={K}", flush=True)
+        L.sigma_delta_schedule(segs, B, K, bank_stride=stride)
+        for s_, w in zip(segs, ws):
+            want = OSD.reverse_tail_schedule(w, B, K)
+            got = host(s_["codes"])
+            for b in range(B + K):
+                assert_bytes_equal(got[b, :w.size // 2].reshape(w.shape[0], -1), packed(want[b]), f"B={B} K={K} bank {b}")
+
+
+def test_sigma_delta_reverse_tail_looped_core_full_size():
+    # the 13 linears of the looped core, 4 nearest-code + 28 tail accesses
+    wl = synth.looped_sigma_delta(tokens=8)
+    ws = [wl.arrays[f"w{i}"] for i in range(13)]
+    segs, _ = _sd_segments(ws)
+    B, K = 4, 28
+    stride = -(-max(w.size // 2 for w in ws) // 16) * 16
+    for s_ in segs:
+        s_["codes"] = torch.empty((B + K, stride), dtype=torch.uint8, device=s_["w"].device)
+        s_["residue"] = None
+    print("reverse-tail schedule, looped core", flush=True)
+    L = fp4q()
+    L.sigma_delta_schedule(segs, B, K, bank_stride=stride)
+    for i, (s_, w) in enumerate(zip(segs, ws)):
+        rows = sample_rows(w.shape[0], k=6, seed=i)
+        st = ONV.tensor_scale_from_amax(np.abs(w).max())
+        want = OSD.reverse_tail_schedule(w[rows], B, K, tensor_scale=st)
+        got = host(s_["codes"])
+        for b in (0, B - 1, B, B + 7, B + K - 1):
+            bank = got[b, :w.size // 2].reshape(w.shape[0], -1)[rows]
+            assert_bytes_equal(bank, packed(want[b]), f"linear {i} bank {b}")
