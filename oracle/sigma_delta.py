@@ -38,6 +38,7 @@ from typing import Callable, List, Sequence, Tuple
 import numpy as np
 
 from .formats import e2m1_round, e2m1_decode, e4m3_decode
+from .philox import philox4x32
 from . import nvfp4
 
 F32 = np.float32
@@ -133,3 +134,66 @@ def reverse_tail_schedule(w: np.ndarray, n_rtn: int, n_tail: int, tensor_scale=N
     order."""
     chain = sigma_delta_nvfp4(w, n_tail, tensor_scale=tensor_scale, rule=rule)["codes"]
     return [chain[0].copy() for _ in range(n_rtn)] + [c.copy() for c in chain[::-1]]
+
+
+# --------------------------------------------------- stochastic rounding ----
+#: the 15 distinct E2M1 values in increasing order
+E2M1_GRID = np.array([-6.0, -4.0, -3.0, -2.0, -1.5, -1.0, -0.5, 0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def sr_round(x: np.ndarray, words: np.ndarray) -> np.ndarray:
+    """Stochastic rounding of float32 x in [-6, 6] to E2M1 codes with one
+    uint32 random word per element (loopquant page, section 2: a fresh
+    random code per access whose expectation is the weight).  With lo the
+    largest grid value <= x, hi the next one and u = (word >> 8) / 2^24,
+    the code is hi exactly when lo + u (hi - lo) < x (evaluated exactly: in
+    float64 both sides are exact), so P(hi) = (x - lo) / (hi - lo) up to
+    2^-24; x on the grid (and x = 6) is kept.  A zero value keeps the sign
+    bit of x, as the nearest-code quantizer does."""
+    x = np.asarray(x, dtype=F32)
+    x64 = x.astype(np.float64)
+    li = np.searchsorted(E2M1_GRID, x64, side="right") - 1
+    li = np.clip(li, 0, E2M1_GRID.size - 1)
+    hi_i = np.minimum(li + 1, E2M1_GRID.size - 1)
+    lo, hi = E2M1_GRID[li], E2M1_GRID[hi_i]
+    u = (np.asarray(words, dtype=np.uint32) >> np.uint32(8)).astype(np.float64) * 2.0 ** -24
+    t = lo + u * (hi - lo)                                     # exact
+    v = np.where((li < E2M1_GRID.size - 1) & (t < x64), hi, lo)
+    mag = np.searchsorted(E2M1_VALUES_POS, np.abs(v)).astype(np.uint8)
+    neg = (v < 0) | ((v == 0) & np.signbit(x))
+    return mag | (neg.astype(np.uint8) << 3)
+
+
+E2M1_VALUES_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def sr_words(rows, cols: int, step: int, seed: int, segment: int = 0) -> np.ndarray:
+    """Random word of each element of the given rows (row-major index
+    e = row * cols + col) at one access: Philox4x32-10 with counter
+    (g mod 2^32, g div 2^32, step mod 2^32, segment) for g = e div 4, key
+    (seed mod 2^32, seed div 2^32 mod 2^32); element e takes output word
+    e mod 4.  Returns uint32 [len(rows), cols]."""
+    e = np.asarray(rows, dtype=np.uint64)[:, None] * np.uint64(cols) + np.arange(cols, dtype=np.uint64)[None, :]
+    g = e >> np.uint64(2)
+    out = philox4x32(g & np.uint64(0xFFFFFFFF), g >> np.uint64(32), int(step) & 0xFFFFFFFF, int(segment),
+                     int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF)
+    stacked = np.stack(out, axis=-1)                          # [rows, cols, 4]
+    return np.take_along_axis(stacked, (e & np.uint64(3)).astype(np.int64)[..., None], axis=-1)[..., 0]
+
+
+def stochastic_rounding_nvfp4(w: np.ndarray, steps: int, seed: int, step0: int = 0, segment: int = 0,
+                              rows=None, tensor_scale=None, rule: str = "6"):
+    """Code banks of ``steps`` accesses with stochastic rounding at the same
+    fixed NVFP4 scale as the Sigma-Delta chain (x = clamp(W / s, -6, 6));
+    access k draws its words at step step0 + k.  ``rows`` selects rows of
+    the result (the words still follow the full weight's element indexes).
+    Returns a list of uint8 [R, K] unpacked code arrays."""
+    x, _, _, zero = normalised_weight(w, tensor_scale, rule)
+    R, K = x.shape
+    sel = np.arange(R) if rows is None else np.asarray(rows)
+    out = []
+    for k in range(steps):
+        codes = sr_round(x[sel], sr_words(sel, K, step0 + k, seed, segment))
+        codes[zero[sel]] = 0
+        out.append(codes)
+    return out

@@ -192,3 +192,69 @@ def test_reverse_tail_schedule():
     q_int = lambda v: Fraction(math.floor(v + Fraction(1, 2)))
     qs, _ = SD.sigma_delta_exact(Fraction(3, 10), q_int, 8)
     assert [int(q) for q in qs[::-1]] == [0, 0, 0, 1, 0, 0, 1, 0]
+
+
+# ------------------------------------------------- stochastic rounding ----
+
+def test_philox_known_answer_vectors():
+    from oracle.philox import philox4x32
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+    n = 0
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            v = [int(t, 16) for t in line.split()]
+            got = [int(a) for a in philox4x32(*v[:4], v[4], v[5])]
+            assert got == v[6:], line
+            n += 1
+    assert n == 3
+
+
+def test_sr_decision_boundaries():
+    # x = 0.6 between 0.5 and 1: P(hi) = 0.2, hi exactly when u < 0.2
+    b = int(0.2 * 2 ** 24)                        # 3355443.2 -> u = 3355443 / 2^24 < 0.2
+    words = np.array([b << 8, (b + 1) << 8, 0, 0xFFFFFFFF], np.uint32)
+    x = np.full(4, 0.6, np.float32)
+    got = F.e2m1_decode(SD.sr_round(x, words))
+    assert list(got) == [1.0, 0.5, 1.0, 0.5]
+    # exactly at the threshold (t == x) the lower value is kept
+    x = np.array([0.75], np.float32)              # p = 0.5
+    assert F.e2m1_decode(SD.sr_round(x, np.array([(1 << 23) << 8], np.uint32)))[0] == 0.5
+    assert F.e2m1_decode(SD.sr_round(x, np.array([((1 << 23) - 1) << 8], np.uint32)))[0] == 1.0
+    # grid points, the ends and signed zeros are kept whatever the word
+    grid = np.array([-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    for word in (0, 0x12345678, 0xFFFFFFFF):
+        c = SD.sr_round(grid, np.full(grid.size, word, np.uint32))
+        np.testing.assert_array_equal(F.e2m1_decode(c), grid)
+    assert SD.sr_round(np.array([-0.0], np.float32), np.array([0], np.uint32))[0] == 0x8
+    assert SD.sr_round(np.array([-0.2], np.float32), np.array([0], np.uint32))[0] == 0x8            # -0.2 up to -0
+    assert SD.sr_round(np.array([-0.2], np.float32), np.array([0xFFFFFFFF], np.uint32))[0] == 0x9   # or down to -0.5
+
+
+def test_sr_is_unbiased_and_brackets_x():
+    rng = np.random.default_rng(45)
+    x = rng.uniform(-6, 6, 64).astype(np.float32)
+    n = 4096
+    vals = np.stack([F.e2m1_decode(SD.sr_round(x, SD.sr_words([0], 64, k, 7)[0])) for k in range(n)])
+    lo = SD.E2M1_GRID[np.searchsorted(SD.E2M1_GRID, x.astype(np.float64), side="right") - 1]
+    assert np.all((vals == lo) | (vals > lo))
+    assert np.all(vals <= lo + 2.0)
+    gap = np.diff(SD.E2M1_GRID).max()
+    # |mean - x| within 6 standard errors (sd <= gap / 2)
+    assert np.all(np.abs(vals.mean(axis=0) - x) <= 6 * (gap / 2) / np.sqrt(n))
+
+
+def test_sr_words_counter_layout():
+    # four consecutive elements share one Philox call (output words 0..3);
+    # steps, segments and seeds give different streams; a row's words do not
+    # depend on which other rows are drawn
+    from oracle.philox import philox4x32
+    w = SD.sr_words([0, 1], 8, 3, 0x1_0000_0002, segment=5)
+    ref = philox4x32(np.arange(4), 0, 3, 5, 2, 1)
+    np.testing.assert_array_equal(w.reshape(-1), np.stack(ref, axis=-1).reshape(-1))
+    assert not np.array_equal(SD.sr_words([0], 64, 0, 7), SD.sr_words([0], 64, 1, 7))
+    assert not np.array_equal(SD.sr_words([0], 64, 0, 7, 1), SD.sr_words([0], 64, 0, 7, 0))
+    np.testing.assert_array_equal(SD.sr_words([3, 9], 16, 2, 11)[1], SD.sr_words([9], 16, 2, 11)[0])
+    ws = synth.normal_f32(46, (12, 64), 0.02)
+    full = SD.stochastic_rounding_nvfp4(ws, 2, seed=9)
+    part = SD.stochastic_rounding_nvfp4(ws, 2, seed=9, rows=[4, 11])
+    np.testing.assert_array_equal(full[1][[4, 11]], part[1])
