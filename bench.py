@@ -428,6 +428,11 @@ def run_extras(L, synth, np, torch, dev, stream, log):
 
     sd["multibank_R32_one_launch"] = _bw(_time_op(torch, stream, multibank, 10), nw * (4 + 4 + 4 + 0.5 * R + 1 / 16))
     sd["reverse_tail_16_plus_16_one_launch"] = _bw(_time_op(torch, stream, schedule, 10), nw * (4 + 0.5 * R + 1 / 16))
+
+    def stochastic(_):
+        L.stochastic_round_requant(msegs, R, seed=42, bank_stride=stride)
+
+    sd["stochastic_rounding_R32_one_launch"] = _bw(_time_op(torch, stream, stochastic, 10), nw * (4 + 0.5 * R + 1 / 16))
     del banks, msegs
     ex["looped_sigma_delta_13x_R32"] = sd
     del segs, gem

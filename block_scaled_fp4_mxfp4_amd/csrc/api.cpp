@@ -221,6 +221,29 @@ int fp4q_sigma_delta_schedule(const fp4q_sd_segment* segs, int nseg, int n_rtn, 
                        "sigma_delta_schedule");
 }
 
+int fp4q_stochastic_round_requant(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes,
+                                  uint64_t seed, uint32_t step0, void* stream) {
+  g_last_error[0] = 0;
+  if (!segs) return fail(FP4Q_ERR_NULL_PTR, "segs is NULL");
+  if (nseg < 1 || nseg > 64) return fail(FP4Q_ERR_BAD_ARG, "nseg must be in [1, 64]");
+  if (steps < 1 || steps > 4096) return fail(FP4Q_ERR_BAD_ARG, "steps must be in [1, 4096]");
+  for (int i = 0; i < nseg; ++i) {
+    const fp4q_sd_segment& g = segs[i];
+    if (!g.w || !g.scales || !g.tensor_scale || !g.codes)
+      return fail(FP4Q_ERR_NULL_PTR, "segment %d has a NULL pointer", i);
+    if (g.rows <= 0 || g.cols <= 0 || g.cols % 16) return fail(FP4Q_ERR_BAD_SHAPE, "segment %d: bad shape", i);
+    if (g.rows * g.cols > (int64_t(1) << 34)) return fail(FP4Q_ERR_BAD_SHAPE, "segment %d: too large", i);
+    if (!aligned16(g.w) || !aligned16(g.codes))
+      return fail(FP4Q_ERR_BAD_ALIGN, "segment %d: w and codes must be 16-byte aligned", i);
+    if (steps > 1 && (bank_stride_bytes < g.rows * g.cols / 2 || bank_stride_bytes % 16))
+      return fail(FP4Q_ERR_BAD_ARG, "segment %d: bank_stride_bytes too small or not a multiple of 16", i);
+  }
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_stochastic_round(segs, nseg, steps, steps > 1 ? bank_stride_bytes : 0, seed,
+                                                     step0, as_stream(stream)),
+                       "stochastic_round_requant");
+}
+
 int fp4q_harmonize_nvfp4(const fp4q_nv_member* members, int n_members,
                          float* shared_tensor_scale, void* stream) {
   g_last_error[0] = 0;

@@ -531,6 +531,105 @@ __global__ __launch_bounds__(kThreads) void k_sigma_delta(const SdArgs args, int
   }
 }
 
+// ------------------------------------------------- stochastic rounding ----
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of
+// (c0..c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
+// with the key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c2 = hi0 ^ c3 ^ k1;
+    c1 = lo1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// Stochastic rounding of x in [-6, 6] to an E2M1 code with one random word:
+// lo = the largest E2M1 value <= x, hi = the next one; u = (word >> 8) 2^-24;
+// hi exactly when lo + u (hi - lo) < x, which float64 evaluates exactly
+// (hi - lo is a power of two), so P(hi) = (x - lo) / (hi - lo) up to 2^-24.
+// Values on the grid are kept; a zero value keeps the sign bit of x.
+__device__ __forceinline__ uint32_t sr_code(float x, uint32_t word) {
+  const float a = __builtin_fabsf(x);
+  const uint32_t fl = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
+  const uint32_t ce = fl + (e2m1_decode(fl) < a ? 1u : 0u);       // smallest magnitude >= a
+  uint32_t lo_c, hi_c;
+  bool has_hi;
+  if (__float_as_uint(x) >> 31) {                                 // below: -mag(ce); above: -mag(ce - 1)
+    lo_c = ce | 8u; hi_c = (ce - 1u) | 8u; has_hi = ce > 0u;
+  } else {
+    lo_c = fl; hi_c = fl + 1u; has_hi = fl < 7u;
+  }
+  if (!has_hi) return lo_c;
+  const double lo = (double)e2m1_decode(lo_c), hi = (double)e2m1_decode(hi_c);
+  const double t = lo + (double)(word >> 8) * 0x1p-24 * (hi - lo);
+  return t < (double)x ? hi_c : lo_c;
+}
+
+// `steps` accesses of stochastic rounding at the fixed NVFP4 scale of each
+// segment (x = clamp(w / s, -6, 6), as the Sigma-Delta chain), access k
+// written to bank k.  Element e (row-major within its segment) draws output
+// word e mod 4 of Philox4x32-10 at counter (g lo, g hi, step0 + k, segment
+// index) with g = e / 4, key (k0, k1).
+__global__ __launch_bounds__(kThreads) void k_stochastic_round(const SdArgs args, int steps, int64_t bank_stride,
+                                                               uint32_t k0, uint32_t k1, uint32_t step0,
+                                                               int seg_base) {
+  int seg = 0;
+  while (seg + 1 < args.nseg && (int)blockIdx.x >= args.wg_start[seg + 1]) ++seg;
+  const int64_t wg = (int64_t)blockIdx.x - args.wg_start[seg];
+  const int64_t n = args.nchunks[seg];
+  const float st = *args.ts[seg];
+  float x[kSdUnroll][8];
+  int64_t cidx[kSdUnroll];
+  uint32_t sb_raw[kSdUnroll];
+#pragma unroll
+  for (int u = 0; u < kSdUnroll; ++u) {
+    cidx[u] = (wg * kSdUnroll + u) * kThreads + threadIdx.x;
+    const int64_t cl = clamp_chunk(cidx[u], n);
+    load8<false>(args.w[seg], cl * 8, x[u]);
+    sb_raw[u] = args.scales[seg][cl >> 1];
+  }
+#pragma unroll
+  for (int u = 0; u < kSdUnroll; ++u) {
+    const bool in = cidx[u] < n;
+    const float s = st * e4m3_decode(in ? sb_raw[u] : 0u);
+    const float rho = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float xi = in ? x[u][i] * rho : 0.0f;
+      if (!(s != 0.0f)) xi = 0.0f;
+      x[u][i] = fminf(fmaxf(xi, -6.0f), 6.0f);
+    }
+  }
+  uint8_t* codes = args.codes[seg];
+  const uint32_t sid = (uint32_t)(seg_base + seg);
+  for (int k = 0; k < steps; ++k) {
+#pragma unroll
+    for (int u = 0; u < kSdUnroll; ++u) {
+      if (cidx[u] >= n) continue;
+      uint32_t pk = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {                      // two Philox groups of four elements
+        const uint64_t g = (uint64_t)cidx[u] * 2 + h;
+        const uint4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), step0 + (uint32_t)k, sid, k0, k1);
+        pk |= sr_code(x[u][4 * h + 0], r.x) << (16 * h);
+        pk |= sr_code(x[u][4 * h + 1], r.y) << (16 * h + 4);
+        pk |= sr_code(x[u][4 * h + 2], r.z) << (16 * h + 8);
+        pk |= sr_code(x[u][4 * h + 3], r.w) << (16 * h + 12);
+      }
+      reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pk;
+    }
+  }
+}
+
 // ------------------------------------------ fused-member harmonization ----
 // One shared tensor scale for the members of a fused NVFP4 GEMM: s_t is the
 // largest member scale; member i's block scales become the E4M3 value
@@ -790,6 +889,33 @@ hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* share
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_harmonize_cells, dim3(1), dim3(64), 0, s, a, shared);
   return hipGetLastError();
+}
+
+hipError_t launch_stochastic_round(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride,
+                                   uint64_t seed, uint32_t step0, hipStream_t s) {
+  for (int base = 0; base < nseg; base += kSdMaxSeg) {
+    SdArgs a = {};
+    const int cnt = (nseg - base) < kSdMaxSeg ? (nseg - base) : kSdMaxSeg;
+    a.nseg = cnt;
+    int32_t wg = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const fp4q_sd_segment& g = segs[base + i];
+      a.w[i] = g.w;
+      a.scales[i] = g.scales;
+      a.ts[i] = g.tensor_scale;
+      a.res[i] = nullptr;
+      a.codes[i] = g.codes;
+      a.nchunks[i] = g.rows * (g.cols / 8);
+      a.wg_start[i] = wg;
+      wg += (int32_t)grid_for(a.nchunks[i], (int64_t)kThreads * kSdUnroll);
+    }
+    a.wg_start[cnt] = wg;
+    hipLaunchKernelGGL(k_stochastic_round, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride,
+                       (uint32_t)seed, (uint32_t)(seed >> 32), step0, base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fp4q

@@ -51,6 +51,8 @@ _SIGS = {
     "fp4q_balance_scale": ([_p, _i, _l, _l, _l, _p, _i, _l, _l, ctypes.c_double, _p, _p, _p], _i),
     "fp4q_sigma_delta_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, _p], _i),
     "fp4q_sigma_delta_schedule": ([ctypes.POINTER(SdSegment), _i, _i, _i, _l, _p], _i),
+    "fp4q_stochastic_round_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, ctypes.c_uint64, ctypes.c_uint32,
+                                       _p], _i),
     "fp4q_harmonize_nvfp4": ([ctypes.POINTER(NvMember), _i, _p, _p], _i),
     "fp4q_hessian_accumulate": ([_p, _l, _l, _l, _p, _p], _i),
     "fp4q_macaq_workspace_bytes": ([_l, _l], _l),
@@ -261,6 +263,23 @@ def sigma_delta_schedule(segments: Sequence[dict], n_rtn: int, n_tail: int, bank
                            0 if res is None else res.data_ptr(), s["codes"].data_ptr(), w.shape[0], w.shape[1])
     _check(lib.fp4q_sigma_delta_schedule(arr, len(segments), int(n_rtn), int(n_tail), int(bank_stride),
                                          _stream(dev)), "sigma_delta_schedule")
+
+
+def stochastic_round_requant(segments: Sequence[dict], steps: int, seed: int, step0: int = 0,
+                             bank_stride: int = 0) -> None:
+    """Write ``steps`` stochastic-rounding code banks per weight (Philox
+    words keyed by ``seed``, accesses step0 .. step0 + steps - 1).
+    Segments as for :func:`sigma_delta_requant`; ``residue`` is not used."""
+    arr = (SdSegment * len(segments))()
+    dev = None
+    for i, s in enumerate(segments):
+        w = s["w"]
+        dev = w.device
+        arr[i] = SdSegment(w.data_ptr(), s["scales"].data_ptr(), s["tensor_scale"].data_ptr(), 0,
+                           s["codes"].data_ptr(), w.shape[0], w.shape[1])
+    _check(lib.fp4q_stochastic_round_requant(arr, len(segments), int(steps), int(bank_stride),
+                                             int(seed) & ((1 << 64) - 1), int(step0) & 0xFFFFFFFF, _stream(dev)),
+           "stochastic_round_requant")
 
 
 # ----------------------------------------------------------------- GEMM ----

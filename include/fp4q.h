@@ -218,6 +218,28 @@ int fp4q_sigma_delta_schedule(const fp4q_sd_segment* segs, int nseg, int n_rtn, 
                               int64_t bank_stride_bytes, void* stream);
 
 /*
+ * Stochastic-rounding code banks for the looped core, the comparison the
+ * loopquant page runs against Sigma-Delta.  [LQ] section 2 (a fresh random
+ * code per access whose expectation equals the weight) and the experiments
+ * that use one fixed seed for the whole weight trajectory.  Same fixed
+ * scale and x = clamp(w / s, -6, 6) as fp4q_sigma_delta_requant; per
+ * element, lo = the largest E2M1 value <= x, hi = the next one,
+ * u = (word >> 8) * 2^-24: the code is hi exactly when lo + u (hi - lo) < x
+ * (exact in float64), so P(hi) = (x - lo) / (hi - lo) up to 2^-24; values
+ * on the grid are kept; a zero value keeps the sign bit of x; zero-scale
+ * blocks give code 0.
+ * Random words: Philox4x32-10 (Salmon et al., SC'11) with key
+ * (seed mod 2^32, seed >> 32); element e (row-major within segment i) at
+ * access k takes output word e mod 4 of counter
+ * (g mod 2^32, g >> 32, step0 + k, i), g = e / 4.
+ * Access k is written at segs[i].codes + k * bank_stride_bytes (ignored when
+ * steps == 1, else >= rows*cols/2 and a multiple of 16).  The residue field
+ * is not used.  steps in [1, 4096], nseg in [1, 64].
+ */
+int fp4q_stochastic_round_requant(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes,
+                                  uint64_t seed, uint32_t step0, void* stream);
+
+/*
  * One member of a fused NVFP4 GEMM (weights quantized separately and
  * concatenated along N).  The ARRAY of members lives in HOST memory; the
  * pointers inside it are device pointers.

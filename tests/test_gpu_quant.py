@@ -421,3 +421,50 @@ def test_sigma_delta_reverse_tail_looped_core_full_size():
         for b in (0, B - 1, B, B + 7, B + K - 1):
             bank = got[b, :w.size // 2].reshape(w.shape[0], -1)[rows]
             assert_bytes_equal(bank, packed(want[b]), f"linear {i} bank {b}")
+
+
+def _sr_segments(ws, steps):
+    segs, _ = _sd_segments(ws)
+    stride = -(-max(w.size // 2 for w in ws) // 16) * 16
+    for s_ in segs:
+        s_["codes"] = torch.empty((steps, stride), dtype=torch.uint8, device=s_["w"].device)
+        s_["residue"] = None
+    return segs, stride
+
+
+def test_stochastic_rounding_small_segments_bit_exact():
+    # 18 segments: two launches of the segment table, so the segment index
+    # in the Philox counter must continue across them
+    shapes = [(48, 64), (16, 128), (7, 32)] * 6
+    ws = [synth.normal_f32(140 + i, shp, 0.02) for i, shp in enumerate(shapes)]
+    ws[0][5, 16:32] = 0.0
+    ws[1][2, :16] = -0.0
+    segs, stride = _sr_segments(ws, 5)
+    print("stochastic rounding, 18 segments x 5 accesses", flush=True)
+    L = fp4q()
+    L.stochastic_round_requant(segs, 5, seed=42, step0=7, bank_stride=stride)
+    for i, (s_, w) in enumerate(zip(segs, ws)):
+        st = ONV.tensor_scale_from_amax(np.abs(w).max())
+        want = OSD.stochastic_rounding_nvfp4(w, 5, 42, step0=7, segment=i, tensor_scale=st)
+        got = host(s_["codes"])
+        for k in range(5):
+            assert_bytes_equal(got[k, :w.size // 2].reshape(w.shape[0], -1), packed(want[k]), f"segment {i} access {k}")
+
+
+def test_stochastic_rounding_looped_core_full_size():
+    wl = synth.looped_sigma_delta(tokens=8)
+    ws = [wl.arrays[f"w{i}"] for i in range(13)]
+    R = 32
+    segs, stride = _sr_segments(ws, R)
+    print("stochastic rounding, looped core, 32 accesses", flush=True)
+    L = fp4q()
+    seed = 0x5EED_0000_002A
+    L.stochastic_round_requant(segs, R, seed=seed, bank_stride=stride)
+    for i, (s_, w) in enumerate(zip(segs, ws)):
+        rows = sample_rows(w.shape[0], k=6, seed=i)
+        st = ONV.tensor_scale_from_amax(np.abs(w).max())
+        want = OSD.stochastic_rounding_nvfp4(w, R, seed, segment=i, rows=rows, tensor_scale=st)
+        got = host(s_["codes"])
+        for k in (0, 1, 17, R - 1):
+            bank = got[k, :w.size // 2].reshape(w.shape[0], -1)[rows]
+            assert_bytes_equal(bank, packed(want[k]), f"linear {i} access {k}")
