@@ -31,6 +31,7 @@
 
 #include <atomic>
 #include <stdint.h>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -49,6 +50,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
@@ -191,7 +193,13 @@ struct MxLayout {
 };
 
 // NW wavefronts in a (NW / 2) x 2 grid over the tile; NS ring slots.
-template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS>
+// M32 = 1: 32 x 32 matrix instructions (v_mfma_scale_f32_32x32x64_f8f6f4,
+// v_mfma_f32_32x32x16_f16), which sustain about twice the rate of the
+// 16 x 16 shapes on gfx950 (measured: 9.4 vs 5.0 PFLOP/s for FP4, 2.4 vs
+// 1.4 for fp16 with independent accumulators); lane l then serves row
+// l % 32 and K half l / 32, and accumulator register r holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS, int M32>
 __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   constexpr int NT = NW * 64;
   using Lay = MxLayout<FMT, BM, BN, CB, NT>;
@@ -200,7 +208,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   constexpr int WM = NW / 2, RW = BM / WM;        // wavefront rows, rows per wavefront
   static_assert(BM % 64 == 0 && BM <= 512 && BN % 32 == 0 && BN <= 320 && (CB == 64 || CB == 128), "tile");
   static_assert((NW == 4 || NW == 8) && NS >= 2 && NS <= 4 && RW % 16 == 0, "layout");
-  constexpr int FM = RW / 16, FN = BN / 32;
+  static_assert(!M32 || (RW % 32 == 0 && (BN / 2) % 32 == 0 && FMT != FMT_W16), "32 x 32 tiles");
+  constexpr int TS = M32 ? 32 : 16;               // accumulator tile edge
+  constexpr int FM = RW / TS, FN = BN / (2 * TS);
+  using Acc = typename std::conditional<M32 != 0, v16f, v4f>::type;
   // the ring, and after the K loop the epilogue's 16-row staging strips
   constexpr int EPI = NW * 16 * (BN / 2 + 4) * 4;
   constexpr int SMEM = NS * Lay::STAGE > EPI ? NS * Lay::STAGE : EPI;
@@ -208,6 +219,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
+  const int r32 = lane & 31, hh = lane >> 5;      // 32 x 32 instructions: row, K half
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -291,11 +303,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 #pragma unroll
   for (int i = 0; i < Lay::SB_LD; ++i) nload += (i * NT + wave * 64 < Lay::SB_N);
 
-  v4f acc[FM][FN];
+  Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
 
   // Stage kt lives in ring slot kt % NS, and NS - 1 stages are loaded
   // ahead.  At the top of iteration kt the wait leaves only the later
@@ -313,7 +325,43 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     if (kt + NS - 1 < KT) issue(kt + NS - 1);
-    if constexpr (FMT == FMT_MX) {
+    if constexpr (FMT == FMT_MX && M32) {
+      // Step ks covers K elements [64 ks, 64 ks + 64) of the stage; lane half
+      // hh reads 16-byte chunk 2 ks + hh of its row: one 32-element MXFP4
+      // block, whose scale byte has the same index.  A fragments first, then
+      // the B fragments one column block ahead of their multiplies.
+      const uint8_t* st = smem + (kt % NS) * Lay::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < CB / 32; ++ks) {
+        const int c = 2 * ks + hh;
+        v8i fa[FM];
+        int fsa[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm * RW + i * 32 + r32;
+          const uint4 q = *reinterpret_cast<const uint4*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+          fa[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          fsa[i] = st[Lay::SA_OFF + row * Lay::SCB + c];
+        }
+        auto ldb = [&](int j, v8i& fb, int& fsb) {
+          const int row = wn * (BN / 2) + j * 32 + r32;
+          const uint4 q = *reinterpret_cast<const uint4*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+          fb = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          fsb = st[Lay::SB_OFF + row * Lay::SCB + c];
+        };
+        v8i fb[2];
+        int fsb[2];
+        ldb(0, fb[0], fsb[0]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (j + 1 < FN) ldb(j + 1, fb[(j + 1) & 1], fsb[(j + 1) & 1]);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j & 1], acc[i][j], 4, 4, 0, fsa[i],
+                                                                        0, fsb[j & 1]);
+        }
+      }
+    } else if constexpr (FMT == FMT_MX) {
       // Instruction step ks covers K elements [128 ks, 128 ks + 128) of the
       // stage; lane group g reads 16-byte chunk 4 ks + g of its row.  The A
       // fragments of the step are read first, then the B fragments one
@@ -391,6 +439,59 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
           }
         }
       }
+    } else if constexpr (M32) {
+      // NVFP4, 32 x 32 x 16 fp16 instructions: step ks covers K elements
+      // [64 ks, 64 ks + 64) of the stage; lane half hh reads 16-byte chunk
+      // c = 2 ks + hh of its row (two 16-element blocks, scale bytes 2c and
+      // 2c + 1) and feeds its dwords t = 0..3 (8 elements each) to
+      // instruction t; A and B use the same assignment, so each instruction
+      // sums over matching K elements.
+      const uint8_t* st = smem + (kt % NS) * Lay::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < CB / 32; ++ks) {
+        const int c = 2 * ks + hh;
+        uint4 qa[FM];
+        v2h sa[FM][2];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm * RW + i * 32 + r32;
+          qa[i] = *reinterpret_cast<const uint4*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+          const uint32_t b2 = *reinterpret_cast<const uint16_t*>(st + Lay::SA_OFF + row * Lay::SCB + 2 * c);
+          const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 1.0f, false));
+          sa[i][0] = v2h{t[0], t[0]};
+          sa[i][1] = v2h{t[1], t[1]};
+        }
+        uint4 qb[FN];
+        v2h sb[FN][2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * (BN / 2) + j * 32 + r32;
+          qb[j] = *reinterpret_cast<const uint4*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+          const uint32_t b2 = *reinterpret_cast<const uint16_t*>(st + Lay::SB_OFF + row * Lay::SCB + 2 * c);
+          const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 1.0f, false));
+          sb[j][0] = v2h{t[0], t[0]};
+          sb[j][1] = v2h{t[1], t[1]};
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v8h ha[FM];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const uint32_t w = t == 0 ? qa[i].x : t == 1 ? qa[i].y : t == 2 ? qa[i].z : qa[i].w;
+            ha[i] = dequant8(w, sa[i][t >> 1]);
+          }
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const uint32_t w = t == 0 ? qb[j].x : t == 1 ? qb[j].y : t == 2 ? qb[j].z : qb[j].w;
+            const v8h hb = dequant8(w, sb[j][t >> 1]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], hb, acc[i][j], 0, 0, 0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }
     } else {
       // NVFP4: lane group g owns elements [32 c, 32 c + 32) of chunk c; each
       // half h is one 16-element block, consumed as two 8-element slices by
@@ -455,17 +556,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   const int64_t col0 = n0 + wn * WC;
   const bool vec = ((p.ldy & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.Y) & 15) == 0);
   const float tsc = FMT == FMT_NV ? (*p.Ats) * (*p.Bts) : FMT == FMT_W16 ? *p.Bts : 1.0f;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = acc[i][j][r];
-        if constexpr (FMT != FMT_MX) v = v * tsc;
-        stage[(g * 4 + r) * LDE + j * 16 + r16] = v;
-      }
-    const int64_t row0 = m0 + wm * RW + i * 16;
+  // writes the 16 x WC strip staged in `stage` to output rows row0 .. +15
+  auto write_strip = [&](int64_t row0) {
 #pragma unroll
     for (int k = 0; k < (16 * WC / 4 + 63) / 64; ++k) {
       const int idx = k * 64 + lane;
@@ -490,11 +582,48 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
         }
       }
     }
+  };
+  if constexpr (M32) {
+    // 32-row tiles leave as two 16-row strips: register r of lane l holds
+    // tile row 8 (r / 4) + 4 (l / 32) + r % 4, so strip q takes r in
+    // [8 q, 8 q + 8)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r8 = 0; r8 < 8; ++r8) {
+            float v = acc[i][j][8 * q + r8];
+            if constexpr (FMT != FMT_MX) v = v * tsc;
+            stage[(8 * (r8 >> 2) + 4 * hh + (r8 & 3)) * LDE + j * 32 + r32] = v;
+          }
+        write_strip(m0 + wm * RW + i * 32 + 16 * q);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[i][j][r];
+          if constexpr (FMT != FMT_MX) v = v * tsc;
+          stage[(g * 4 + r) * LDE + j * 16 + r16] = v;
+        }
+      write_strip(m0 + wm * RW + i * 16);
+    }
   }
 }
 
+#ifndef FP4Q_MX_M32
+#define FP4Q_MX_M32 0         // 1: 32 x 32 x 64 FP4 instructions (bit-exact too, but 5-8% slower on the
+                              // 2048 x 14336 x 4096 GEMM at every tile and ring tried: its loop is
+                              // not bound by the instruction rate)
+#endif
 #ifndef FP4Q_MX_BN
-#define FP4Q_MX_BN 256        // workgroup columns (224 for widths that 224 divides and 256 does not)
+#define FP4Q_MX_BN 256        // workgroup columns (16 x 16 path: 224 for widths that 224 divides and 256 does not)
 #endif
 #ifndef FP4Q_MX_BM
 #define FP4Q_MX_BM 256        // workgroup rows
@@ -511,11 +640,19 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 #ifndef FP4Q_MX_NS
 #define FP4Q_MX_NS 2          // LDS ring slots
 #endif
+#ifndef FP4Q_NV_M32
+#define FP4Q_NV_M32 1         // 32 x 32 x 16 fp16 instructions on 256 x 128 tiles: 4-6% faster than
+                              // 16 x 16 x 32 on 256 x 160 (0)
+#endif
 #ifndef FP4Q_NV_BM
 #define FP4Q_NV_BM 256
 #endif
 #ifndef FP4Q_NV_BN
+#if FP4Q_NV_M32
+#define FP4Q_NV_BN 128
+#else
 #define FP4Q_NV_BN 160
+#endif
 #endif
 #ifndef FP4Q_NV_CB
 #define FP4Q_NV_CB 64
@@ -530,12 +667,12 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
 inline int cdiv_i(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 
-template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS>
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS, int M32 = 0>
 hipError_t launch_mx3(const MxArgs& a0, hipStream_t s) {
   MxArgs a = a0;
   a.tiles_m = cdiv_i(a.M, BM);
   a.tiles_n = cdiv_i(a.N, BN);
-  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB, NW, NS>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+  hipLaunchKernelGGL((k_gemm_mx3<FMT, BM, BN, CB, MINB, NW, NS, M32>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
                      dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -569,14 +706,14 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
   // grows with its width, so the width with the smaller rounds x width
   // wins (ties: 256).  For 2048 x 14336: 256 -> 448 tiles, 2 rounds x 256;
   // 224 -> 512 tiles, 2 rounds x 224 (measured 5% faster).
-  if constexpr (FP4Q_MX_BN == 256 && FP4Q_MX_CB == 128) {
+  if constexpr (FP4Q_MX_BN == 256 && FP4Q_MX_CB == 128 && !FP4Q_MX_M32) {
     const int64_t cus = device_cus(), tm = cdiv_i(M, FP4Q_MX_BM);
     const int64_t c256 = cdiv_i(tm * cdiv_i(N, 256), cus) * 256;
     const int64_t c224 = cdiv_i(tm * cdiv_i(N, 224), cus) * 224;
     if (c224 < c256)
       return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
   }
-  return launch_mx3<FMT_MX, FP4Q_MX_BM, FP4Q_MX_BN, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
+  return launch_mx3<FMT_MX, FP4Q_MX_BM, FP4Q_MX_BN, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS, FP4Q_MX_M32>(p, s);
 }
 
 #ifndef FP4Q_W16M_BM
@@ -610,7 +747,7 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a
   if (K % (2 * FP4Q_NV_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
     return launch_gemm_nvfp4_staged(a, as, ats, b, bs, bts, M, N, K, y, ldy, s);
   MxArgs p{a, as, b, bs, ats, bts, M, N, K, y, ldy, 0, 0};
-  return launch_mx3<FMT_NV, FP4Q_NV_BM, FP4Q_NV_BN, FP4Q_NV_CB, 1, FP4Q_NV_NW, FP4Q_NV_NS>(p, s);
+  return launch_mx3<FMT_NV, FP4Q_NV_BM, FP4Q_NV_BN, FP4Q_NV_CB, 1, FP4Q_NV_NW, FP4Q_NV_NS, FP4Q_NV_M32>(p, s);
 }
 
 }  // namespace fp4q
