@@ -402,13 +402,19 @@ def run_extras(L, synth, np, torch, dev, stream, log):
     sd = {"linears": len(shapes), "weights": nw, "R": R}
     sd["sigma_delta_step"] = _bw(_time_op(torch, stream, sd_step, R), nw * (4 + 4 + 4 + 0.5 + 1 / 16))
     sd["w4a16_gemms_per_step"] = _fl(_time_op(torch, stream, gemms, R), flops, "bf16_TFLOPs")
+    gprobs = [(a, c, s_, tsc, yo) for a, c, s_, tsc, yo in gem]
+
+    def gemms_grouped(_):
+        L.gemm_w4a16_grouped(gprobs)
+
+    sd["w4a16_gemms_per_step_one_launch"] = _fl(_time_op(torch, stream, gemms_grouped, R), flops, "bf16_TFLOPs")
 
     def full_forward(_):
         for s_ in segs:
             s_["residue"].zero_()
         for _k in range(R):
             sd_step(0)
-            gemms(0)
+            gemms_grouped(0)
 
     tfw = _time_op(torch, stream, full_forward, 3, warm=1)
     sd["forward_R32_ms"] = round(tfw["median_ms"], 3)

@@ -340,10 +340,9 @@ int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, con
                        "gemm_nvfp4");
 }
 
-int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda, const uint8_t* b_codes, const uint8_t* b_scales,
-                    const float* b_tscale, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
-                    void* stream) {
-  g_last_error[0] = 0;
+namespace {
+int check_w4a16(const void* a_bf16, int64_t lda, const uint8_t* b_codes, const uint8_t* b_scales,
+                const float* b_tscale, int64_t M, int64_t N, int64_t K, const float* y, int64_t ldy) {
   if (!a_bf16 || !b_codes || !b_scales || !b_tscale || !y) return fail(FP4Q_ERR_NULL_PTR, "operand pointer is NULL");
   if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_BAD_SHAPE, "M, N and K must be > 0");
   if (K % 128) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 128");
@@ -352,6 +351,31 @@ int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda, const uint8_t* b_codes, con
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return fail(FP4Q_ERR_BAD_SHAPE, "size too large");
   if (!aligned16(a_bf16) || lda % 8 || !aligned16(b_codes)) return fail(FP4Q_ERR_BAD_ALIGN, "a, lda or b_codes not 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(y) & 3u)) return fail(FP4Q_ERR_BAD_ALIGN, "y must be 4-byte aligned");
+  return FP4Q_OK;
+}
+}  // namespace
+
+int fp4q_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, void* stream) {
+  g_last_error[0] = 0;
+  if (!probs) return fail(FP4Q_ERR_NULL_PTR, "probs is NULL");
+  if (n < 1 || n > 64) return fail(FP4Q_ERR_BAD_ARG, "n must be in [1, 64]");
+  for (int i = 0; i < n; ++i) {
+    const fp4q_w4a16_problem& q = probs[i];
+    if (int st = check_w4a16(q.a_bf16, q.lda, q.b_codes, q.b_scales, q.b_tscale, q.M, q.N, q.K, q.y, q.ldy)) {
+      char msg[sizeof(g_last_error)];
+      std::snprintf(msg, sizeof(msg), "%s", g_last_error);
+      return fail(st, "problem %d: %s", i, msg);
+    }
+  }
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_gemm_w4a16_grouped(probs, n, as_stream(stream)), "gemm_w4a16_grouped");
+}
+
+int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda, const uint8_t* b_codes, const uint8_t* b_scales,
+                    const float* b_tscale, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
+                    void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_w4a16(a_bf16, lda, b_codes, b_scales, b_tscale, M, N, K, y, ldy)) return st;
   if (int st = check_device()) return st;
   return launch_status(fp4q::launch_gemm_w4a16(a_bf16, lda, b_codes, b_scales, b_tscale, M, N, K, y, ldy,
                                                as_stream(stream)),

@@ -199,8 +199,10 @@ struct MxLayout {
 // 1.4 for fp16 with independent accumulators); lane l then serves row
 // l % 32 and K half l / 32, and accumulator register r holds row
 // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS, int M32>
-__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
+// One output tile (index bid of p's tiles) per call; the kernels below
+// map workgroups to (problem, tile).
+template <int FMT, int BM, int BN, int CB, int NW, int NS, int M32>
+__device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
   constexpr int NT = NW * 64;
   using Lay = MxLayout<FMT, BM, BN, CB, NT>;
   constexpr int CPR = CB / 16;                    // 16-byte chunks per staged row
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, r16 = lane & 15;
   const int r32 = lane & 31, hh = lane >> 5;      // 32 x 32 instructions: row, K half
   int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  tile_of(bid, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t ldb = p.K / 2, lds = p.K / (FMT == FMT_MX ? 32 : 16);
   const int KT = (int)(p.K / (2 * CB));
@@ -617,6 +619,27 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
   }
 }
 
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS, int M32>
+__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3(const MxArgs p) {
+  mx3_tile<FMT, BM, BN, CB, NW, NS, M32>(p, (int)blockIdx.x);
+}
+
+// Several problems of one format in one launch: workgroups
+// [start[i], start[i + 1]) take the tiles of problem i.
+constexpr int kMaxGroup = 16;
+struct MxGroup {
+  MxArgs prob[kMaxGroup];
+  int start[kMaxGroup + 1];
+  int n;
+};
+
+template <int FMT, int BM, int BN, int CB, int MINB, int NW, int NS, int M32>
+__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3_grouped(const MxGroup grp) {
+  int i = 0;
+  while (i + 1 < grp.n && (int)blockIdx.x >= grp.start[i + 1]) ++i;
+  mx3_tile<FMT, BM, BN, CB, NW, NS, M32>(grp.prob[i], (int)blockIdx.x - grp.start[i]);
+}
+
 #ifndef FP4Q_MX_M32
 #define FP4Q_MX_M32 0         // 1: 32 x 32 x 64 FP4 instructions (bit-exact too, but 5-8% slower on the
                               // 2048 x 14336 x 4096 GEMM at every tile and ring tried: its loop is
@@ -739,6 +762,46 @@ hipError_t launch_gemm_w4a16_direct(const void* a, int64_t lda, const uint8_t* b
                                     hipStream_t s) {
   MxArgs p{reinterpret_cast<const uint8_t*>(a), nullptr, b, bs, nullptr, bts, M, N, K, y, ldy, 0, 0, lda};
   return launch_mx3<FMT_W16, FP4Q_W16M_BM, FP4Q_W16M_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2>(p, s);
+}
+
+hipError_t launch_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, hipStream_t s) {
+  // problems the direct-load kernel takes go into shared launches (longest
+  // K first, so the longest tiles start first); the rest launch alone
+  int idx[64];
+  int nd = 0;
+  for (int i = 0; i < n; ++i) {
+    const fp4q_w4a16_problem& q = probs[i];
+    if (w4a16_direct_supported(q.lda, q.M, q.N, q.K)) {
+      idx[nd++] = i;
+    } else {
+      const hipError_t e = launch_gemm_w4a16(q.a_bf16, q.lda, q.b_codes, q.b_scales, q.b_tscale, q.M, q.N, q.K,
+                                             q.y, q.ldy, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  for (int a = 1; a < nd; ++a)                     // stable insertion sort by K, descending
+    for (int b = a; b > 0 && probs[idx[b]].K > probs[idx[b - 1]].K; --b) {
+      const int t = idx[b]; idx[b] = idx[b - 1]; idx[b - 1] = t;
+    }
+  for (int base = 0; base < nd; base += kMaxGroup) {
+    MxGroup g = {};
+    g.n = (nd - base) < kMaxGroup ? (nd - base) : kMaxGroup;
+    int wg = 0;
+    for (int k = 0; k < g.n; ++k) {
+      const fp4q_w4a16_problem& q = probs[idx[base + k]];
+      MxArgs& a = g.prob[k];
+      a = MxArgs{reinterpret_cast<const uint8_t*>(q.a_bf16), nullptr, q.b_codes, q.b_scales, nullptr, q.b_tscale,
+                 q.M, q.N, q.K, q.y, q.ldy, cdiv_i(q.M, FP4Q_W16M_BM), cdiv_i(q.N, FP4Q_W16M_BN), q.lda};
+      g.start[k] = wg;
+      wg += a.tiles_m * a.tiles_n;
+    }
+    g.start[g.n] = wg;
+    hipLaunchKernelGGL((k_gemm_mx3_grouped<FMT_W16, FP4Q_W16M_BM, FP4Q_W16M_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2, 0>),
+                       dim3((unsigned)wg), dim3(FP4Q_W16M_NW * 64), 0, s, g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* ats,

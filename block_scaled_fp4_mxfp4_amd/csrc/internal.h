@@ -66,6 +66,9 @@ hipError_t launch_gemm_w4a16_direct(const void* a, int64_t lda, const uint8_t* b
 hipError_t launch_gemm_w4a16(const void* a, int64_t lda, const uint8_t* b, const uint8_t* bs,
                              const float* bts, int64_t M, int64_t N, int64_t K, float* y,
                              int64_t ldy, hipStream_t s);
+// Several W4A16 problems; those the direct-load kernel takes share launches
+// of up to 16 problems (n <= 64).
+hipError_t launch_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, hipStream_t s);
 // Largest K the skinny kernel holds in LDS.
 bool skinny_supported(int64_t K);
 // Skinny NVFP4 GEMM for M <= 16.  If a_bf16 != NULL the activation is

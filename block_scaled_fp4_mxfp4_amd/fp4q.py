@@ -36,6 +36,11 @@ class SdSegment(ctypes.Structure):
                 ("codes", _p), ("rows", _l), ("cols", _l)]
 
 
+class W4A16Problem(ctypes.Structure):
+    _fields_ = [("a_bf16", _p), ("lda", _l), ("b_codes", _p), ("b_scales", _p), ("b_tscale", _p),
+                ("M", _l), ("N", _l), ("K", _l), ("y", _p), ("ldy", _l)]
+
+
 class NvMember(ctypes.Structure):
     _fields_ = [("scales", _p), ("tensor_scale", _p), ("rows", _l), ("cols", _l)]
 
@@ -59,6 +64,7 @@ _SIGS = {
     "fp4q_macaq_refine": ([_p, _l, _l, _l, _p, ctypes.c_double, _i, _p, _p, _p, _p, _l, _p], _i),
     "fp4q_gemm_w4a4": ([_i, _p, _p, _p, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_gemm_w4a16": ([_p, _l, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
+    "fp4q_gemm_w4a16_grouped": ([ctypes.POINTER(W4A16Problem), _i, _p], _i),
     "fp4q_linear_w4a4": ([_p, _l, _p, _i, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -305,6 +311,28 @@ def gemm_w4a16(a: torch.Tensor, b_codes, b_scales, b_ts, out: Optional[torch.Ten
     _check(lib.fp4q_gemm_w4a16(_ptr(a), lda, _ptr(b_codes), _ptr(b_scales), _ptr(b_ts), M, N, K, _ptr(y),
                                y.stride(0), _stream(a.device)), "gemm_w4a16")
     return y
+
+
+def gemm_w4a16_grouped(problems: Sequence[tuple]) -> List[torch.Tensor]:
+    """Several W4A16 GEMMs in as few launches as possible.  Each problem is
+    (a bf16 [M, K], b_codes, b_scales, b_ts) or with a fifth element, the
+    fp32 output; returns the outputs."""
+    arr = (W4A16Problem * len(problems))()
+    outs = []
+    dev = None
+    for i, pr in enumerate(problems):
+        a, bc, bs, bt = pr[:4]
+        M, K, lda = _rows_cols_ld(a)
+        N = bc.shape[0]
+        if a.dtype != torch.bfloat16 or bc.shape[1] * 2 != K:
+            raise ValueError(f"problem {i}: a must be bf16 [M, K] matching B")
+        y = pr[4] if len(pr) > 4 and pr[4] is not None else torch.empty((M, N), dtype=torch.float32, device=a.device)
+        arr[i] = W4A16Problem(a.data_ptr(), lda, bc.data_ptr(), bs.data_ptr(), bt.data_ptr(), M, N, K, y.data_ptr(),
+                              y.stride(0))
+        outs.append(y)
+        dev = a.device
+    _check(lib.fp4q_gemm_w4a16_grouped(arr, len(problems), _stream(dev)), "gemm_w4a16_grouped")
+    return outs
 
 
 def linear_w4a4(a: torch.Tensor, b_codes, b_scales, b_ts, a_tscale: Optional[torch.Tensor] = None,

@@ -353,6 +353,34 @@ int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda,
                     int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream);
 
 /*
+ * One W4A16 problem for fp4q_gemm_w4a16_grouped: the arguments of
+ * fp4q_gemm_w4a16 (same meaning, layout and alignment rules).  The ARRAY
+ * lives in HOST memory; the pointers inside it are device pointers.
+ */
+typedef struct fp4q_w4a16_problem {
+  const void* a_bf16;
+  int64_t lda;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* b_tscale;
+  int64_t M, N, K;
+  float* y;
+  int64_t ldy;
+} fp4q_w4a16_problem;
+
+/*
+ * n independent W4A16 GEMMs (the linears of one loop step of the looped
+ * core, [LQ] section 4's W4A16 forward), each exactly as
+ * fp4q_gemm_w4a16 computes it (bit-identical results), in as few launches
+ * as the shapes allow: problems of up to 16 at a time share one launch, so
+ * small GEMMs do not each leave the chip idle at their tail.  Outputs must
+ * not overlap each other or any input.  n in [1, 64]; each problem is
+ * validated as fp4q_gemm_w4a16 validates it (the status names the first
+ * bad problem in fp4q_last_error).
+ */
+int fp4q_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, void* stream);
+
+/*
  * Decode-shaped NVFP4 W4A4 linear with the activation quantization fused
  * into the GEMM ([GDN] "Limitations": decode was slowed by the small-batch
  * NVFP4 activation-quantization kernel).  Quantizes A (bf16) exactly as

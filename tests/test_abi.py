@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fp4q_sigma_delta_requant", "fp4q_gemm_w4a4", "fp4q_gemm_w4a16", "fp4q_linear_w4a4",
               "fp4q_balance_scale", "fp4q_harmonize_nvfp4", "fp4q_hessian_accumulate",
               "fp4q_macaq_workspace_bytes", "fp4q_macaq_refine", "fp4q_sigma_delta_schedule",
-              "fp4q_stochastic_round_requant",
+              "fp4q_stochastic_round_requant", "fp4q_gemm_w4a16_grouped",
               "fp4q_abi_version", "fp4q_status_str",
               "fp4q_last_error"]:
         assert n in names
@@ -158,3 +158,16 @@ def test_macaq_validation(fp4q):
     assert call(lam=-1.0) == 5 and call(lam=float("nan")) == 5 and call(k=-1) == 5
     assert call(wsb=ws - 8) == 5
     assert b"workspace" in L.fp4q_last_error()
+
+
+def test_w4a16_grouped_validation(fp4q):
+    L, P = fp4q.lib, fp4q.W4A16Problem
+    f16 = 0x10000
+    good = P(f16, 128, f16, f16, f16, 4, 4, 128, f16, 4)
+    bad = P(f16, 100, f16, f16, f16, 4, 4, 128, f16, 4)               # lda < K
+    assert L.fp4q_gemm_w4a16_grouped(None, 1, None) == 1
+    assert L.fp4q_gemm_w4a16_grouped((P * 1)(good), 0, None) == 5
+    assert L.fp4q_gemm_w4a16_grouped((P * 2)(good, bad), 2, None) == 2
+    assert b"problem 1" in L.fp4q_last_error()
+    nul = P(f16, 128, 0, f16, f16, 4, 4, 128, f16, 4)
+    assert L.fp4q_gemm_w4a16_grouped((P * 2)(good, nul), 2, None) == 1

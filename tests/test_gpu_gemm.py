@@ -240,3 +240,33 @@ def test_nvfp4_gemm_subnormal_block_scales(M):
         yf, _ = L.linear_w4a4(dev_bf16(xb), bc, bs, bt)
         cxb, sxb, txb = ONV.quantize(OF.bf16_bits_to_f32(xb))
         _check(host(yf), OG.w4a4_nvfp4(cxb, sxb, txb, cw, sw, tw), f"decode subnormal scales M={M}")
+
+
+def test_w4a16_grouped_equals_single_launches():
+    # the looped core's 13 linears at one loop step (hidden and the wider
+    # down-projection input) plus ragged problems; one grouped call gives
+    # the bytes of the 13 + 3 single calls
+    L = fp4q()
+    wl = synth.looped_sigma_delta(tokens=8)
+    h = dev_bf16(wl.arrays["h_bf16"])
+    hd = dev_bf16(wl.arrays["hd_bf16"])
+    probs = []
+    for i, (n, k) in enumerate(wl.meta["shapes"]):
+        c, sc, ts = L.quantize_nvfp4(dev_f32(wl.arrays[f"w{i}"]))
+        probs.append(((hd if k == 3072 else h), c, sc, ts))
+    for M, N, K in ((130, 200, 384), (1, 70, 256), (64, 256, 1024)):
+        a = dev_bf16(synth.f32_to_bf16_bits(synth.heavy_tailed_f32(700 + M, 701, (M, K))))
+        c, sc, ts = L.quantize_nvfp4(dev_f32(synth.normal_f32(702 + N, (N, K), 0.02)))
+        probs.append((a, c, sc, ts))
+    print(f"grouped W4A16: {len(probs)} problems", flush=True)
+    got = [host(y) for y in L.gemm_w4a16_grouped(probs)]
+    for i, pr in enumerate(probs):
+        want = host(L.gemm_w4a16(*pr))
+        assert np.array_equal(got[i].view(np.uint32), want.view(np.uint32)), f"problem {i}"
+    # and one of them against the oracle
+    a, c, sc, ts = probs[-3]
+    xb = synth.f32_to_bf16_bits(synth.heavy_tailed_f32(830, 701, (130, 384)))
+    w = synth.normal_f32(902, (200, 384), 0.02)
+    cw, sw, tw = ONV.quantize(w)
+    ref = OG.matmul_nt(OF.bf16_bits_to_f32(xb).astype(np.float64), ONV.dequantize(cw, sw, tw))
+    _check(got[-3], ref, "grouped W4A16 130x200x384")
