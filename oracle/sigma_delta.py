@@ -33,6 +33,7 @@ Two forms are provided:
 from __future__ import annotations
 
 from fractions import Fraction
+import math
 from typing import Callable, List, Sequence, Tuple
 
 import numpy as np
@@ -196,4 +197,47 @@ def stochastic_rounding_nvfp4(w: np.ndarray, steps: int, seed: int, step0: int =
         codes = sr_round(x[sel], sr_words(sel, K, step0 + k, seed, segment))
         codes[zero[sel]] = 0
         out.append(codes)
+    return out
+
+
+# ------------------------------------------------------------------ F4b ----
+
+def two_point_code(x: float, k: int) -> int:
+    """Access k (k >= 1) of the stateless two-point chain (F4b) for one
+    normalised float32 value x in [-6, 6], in exact rationals.
+
+    The loopquant page names F4b, the "two-point closed-form difference"
+    used in its code-generation microbenchmark, but gives no formula; the
+    reading taken (recorded in the design notes): with lo the largest E2M1
+    value <= x, hi the next one and p = (x - lo) / (hi - lo), access k takes
+    hi exactly when floor(k p) - floor((k - 1) p) = 1, else lo, so after m
+    accesses the code sum is m lo + (hi - lo) floor(m p).  Values on the
+    grid (and 6) are kept; a zero value keeps the sign bit of x."""
+    fx = Fraction(float(np.float32(x)))
+    vals = [Fraction(v).limit_denominator(2) for v in E2M1_GRID]
+    li = max(i for i, v in enumerate(vals) if v <= fx)
+    if li == len(vals) - 1 or vals[li] == fx:
+        v = vals[li]
+    else:
+        lo, hi = vals[li], vals[li + 1]
+        p = (fx - lo) / (hi - lo)
+        up = math.floor(k * p) - math.floor((k - 1) * p)
+        v = hi if up == 1 else lo
+    mag = int(np.searchsorted(E2M1_VALUES_POS, abs(float(v))))
+    neg = v < 0 or (v == 0 and np.signbit(np.float32(x)))
+    return mag | (8 if neg else 0)
+
+
+def two_point_nvfp4(w: np.ndarray, accesses, rows=None, tensor_scale=None, rule: str = "6"):
+    """F4b codes of the given accesses (1-based indexes k) at the fixed
+    NVFP4 scale of the Sigma-Delta chain; ``rows`` selects rows.  Returns a
+    dict k -> uint8 [R, K] unpacked codes.  Pure-Python rationals: small
+    inputs only."""
+    x, _, _, zero = normalised_weight(w, tensor_scale, rule)
+    sel = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    out = {}
+    for k in accesses:
+        codes = np.array([[two_point_code(v, k) for v in x[r]] for r in sel], np.uint8)
+        codes[zero[sel]] = 0
+        out[k] = codes
     return out

@@ -258,3 +258,45 @@ def test_sr_words_counter_layout():
     full = SD.stochastic_rounding_nvfp4(ws, 2, seed=9)
     part = SD.stochastic_rounding_nvfp4(ws, 2, seed=9, rows=[4, 11])
     np.testing.assert_array_equal(full[1][[4, 11]], part[1])
+
+
+# ----------------------------------------------------------------- F4b ----
+
+def test_two_point_chain_pins():
+    # p = 1/2 alternates lo, hi; grid points and the ends are kept
+    assert [SD.two_point_code(0.75, k) for k in range(1, 7)] == [0x1, 0x2] * 3
+    for x in (0.0, 0.5, 1.5, 4.0, 6.0, -6.0, -3.0):
+        want = F.e2m1_round(np.array([x], np.float32))[0]
+        assert all(SD.two_point_code(x, k) == want for k in (1, 2, 5, 100))
+    # x = 0.3 on [0, 0.5] is p = 0.6: floor(0.6 k) - floor(0.6 (k - 1))
+    assert [SD.two_point_code(0.3, k) & 7 for k in range(1, 6)] == [0, 1, 0, 1, 1]
+    # negative side, hi = -0: x = -0.125 in [-0.5, 0], p = 0.75
+    assert [SD.two_point_code(-0.125, k) for k in range(1, 6)] == [0x9, 0x8, 0x8, 0x8, 0x9]
+    # the section 2.1 worked example's p = 0.3 on the integer grid, in the same
+    # closed form, gives 0,0,0,1,0,0,1,0
+    seq = [math.floor(Fraction(3, 10) * k) - math.floor(Fraction(3, 10) * (k - 1)) for k in range(1, 9)]
+    assert seq == [0, 0, 0, 1, 0, 0, 1, 0]
+
+
+def test_two_point_chain_sum_and_brackets():
+    # after m accesses the code sum is m lo + (hi - lo) floor(m p): the prefix
+    # error lies in (-(hi - lo), 0]; every code is lo or hi
+    rng = np.random.default_rng(47)
+    xs = rng.uniform(-6, 6, 40).astype(np.float32)
+    for x in xs:
+        fx = Fraction(float(x))
+        vals = [Fraction(v).limit_denominator(2) for v in SD.E2M1_GRID]
+        li = max(i for i, v in enumerate(vals) if v <= fx)
+        lo = vals[li]
+        hi = vals[min(li + 1, len(vals) - 1)]
+        tot = Fraction(0)
+        for m in range(1, 65):
+            v = Fraction(float(F.e2m1_decode(np.array([SD.two_point_code(x, m)]))[0]))
+            assert v in (lo, hi)
+            tot += v - fx
+            assert -(hi - lo) < tot <= 0 or (hi == lo and tot == 0)
+    # tiny values next to zero are exact too: x = -2^-140 gives
+    # p = 1 - 2^-139, so access 1 takes lo and the next ones hi (-0)
+    tiny = np.float32(-2.0 ** -140)
+    assert [SD.two_point_code(tiny, k) for k in (1, 2, 3, 1000)] == [0x9, 0x8, 0x8, 0x8]
+    assert [SD.two_point_code(-tiny, k) for k in (1, 2, 1000)] == [0x0, 0x0, 0x0]
