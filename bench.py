@@ -439,6 +439,11 @@ def run_extras(L, synth, np, torch, dev, stream, log):
         L.stochastic_round_requant(msegs, R, seed=42, bank_stride=stride)
 
     sd["stochastic_rounding_R32_one_launch"] = _bw(_time_op(torch, stream, stochastic, 10), nw * (4 + 0.5 * R + 1 / 16))
+
+    def two_point(_):
+        L.two_point_requant(msegs, R, bank_stride=stride)
+
+    sd["two_point_R32_one_launch"] = _bw(_time_op(torch, stream, two_point, 10), nw * (4 + 0.5 * R + 1 / 16))
     del banks, msegs
     ex["looped_sigma_delta_13x_R32"] = sd
     del segs, gem

@@ -221,9 +221,8 @@ int fp4q_sigma_delta_schedule(const fp4q_sd_segment* segs, int nseg, int n_rtn, 
                        "sigma_delta_schedule");
 }
 
-int fp4q_stochastic_round_requant(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes,
-                                  uint64_t seed, uint32_t step0, void* stream) {
-  g_last_error[0] = 0;
+namespace {
+int check_bank_segments(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes) {
   if (!segs) return fail(FP4Q_ERR_NULL_PTR, "segs is NULL");
   if (nseg < 1 || nseg > 64) return fail(FP4Q_ERR_BAD_ARG, "nseg must be in [1, 64]");
   if (steps < 1 || steps > 4096) return fail(FP4Q_ERR_BAD_ARG, "steps must be in [1, 4096]");
@@ -238,9 +237,29 @@ int fp4q_stochastic_round_requant(const fp4q_sd_segment* segs, int nseg, int ste
     if (steps > 1 && (bank_stride_bytes < g.rows * g.cols / 2 || bank_stride_bytes % 16))
       return fail(FP4Q_ERR_BAD_ARG, "segment %d: bank_stride_bytes too small or not a multiple of 16", i);
   }
+  return FP4Q_OK;
+}
+}  // namespace
+
+int fp4q_two_point_requant(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes,
+                           uint32_t step0, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_bank_segments(segs, nseg, steps, bank_stride_bytes)) return st;
+  if ((uint64_t)step0 + (uint64_t)steps >= (uint64_t(1) << 24))
+    return fail(FP4Q_ERR_BAD_ARG, "step0 + steps must be below 2^24");
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_stochastic_round(segs, nseg, steps, steps > 1 ? bank_stride_bytes : 0, 0,
+                                                     step0, 1, as_stream(stream)),
+                       "two_point_requant");
+}
+
+int fp4q_stochastic_round_requant(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes,
+                                  uint64_t seed, uint32_t step0, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_bank_segments(segs, nseg, steps, bank_stride_bytes)) return st;
   if (int st = check_device()) return st;
   return launch_status(fp4q::launch_stochastic_round(segs, nseg, steps, steps > 1 ? bank_stride_bytes : 0, seed,
-                                                     step0, as_stream(stream)),
+                                                     step0, 0, as_stream(stream)),
                        "stochastic_round_requant");
 }
 

@@ -37,8 +37,9 @@ hipError_t launch_balance_scale(const void* w, int w_bf16, int64_t N, int64_t K,
 // then `steps` chain codes in reverse; no residue buffer)
 hipError_t launch_sigma_delta(const fp4q_sd_segment* segs, int nseg, int steps,
                               int64_t bank_stride, int sched, int n_rtn, hipStream_t s);
+// two_point != 0: the stateless two-point chain instead (seed unused)
 hipError_t launch_stochastic_round(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride,
-                                   uint64_t seed, uint32_t step0, hipStream_t s);
+                                   uint64_t seed, uint32_t step0, int two_point, hipStream_t s);
 hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* shared, hipStream_t s);
 hipError_t launch_hessian(const float* x, int64_t T, int64_t n, int64_t ldx, double* h, hipStream_t s);
 hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lam,

@@ -574,11 +574,45 @@ __device__ __forceinline__ uint32_t sr_code(float x, uint32_t word) {
   return t < (double)x ? hi_c : lo_c;
 }
 
+// Access k >= 1 of the stateless two-point chain (F4b): lo, hi the E2M1
+// neighbours of x, p = (x - lo) / (hi - lo); hi exactly when
+// floor(k p) - floor((k - 1) p) = 1.  Exact in float64 for k < 2^24:
+// x - lo is exact in float32 (lo = 0, or Sterbenz: lo <= x <= 2 lo in
+// magnitude) except on (-0.5, 0), where k p = k + 2 k x; 2 k x and k (x - lo)
+// need at most 49 bits, and hi - lo is a power of two.
+__device__ __forceinline__ uint32_t two_point_code(float x, uint32_t k) {
+  const float a = __builtin_fabsf(x);
+  const uint32_t fl = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
+  const uint32_t ce = fl + (e2m1_decode(fl) < a ? 1u : 0u);
+  uint32_t lo_c, hi_c;
+  bool has_hi;
+  if (__float_as_uint(x) >> 31) {
+    lo_c = ce | 8u; hi_c = (ce - 1u) | 8u; has_hi = ce > 0u;
+  } else {
+    lo_c = fl; hi_c = fl + 1u; has_hi = fl < 7u;
+  }
+  if (!has_hi) return lo_c;
+  double fk, fk1;
+  if (hi_c == 8u) {                                   // x in [-0.5, 0): k p = k + 2 k x
+    fk = (double)k + __builtin_floor(2.0 * (double)k * (double)x);
+    fk1 = (double)(k - 1u) + __builtin_floor(2.0 * (double)(k - 1u) * (double)x);
+  } else {
+    const float lo = e2m1_decode(lo_c), d = e2m1_decode(hi_c) - lo;
+    const double y = (double)(x - lo) / (double)d;    // exact
+    fk = __builtin_floor((double)k * y);
+    fk1 = __builtin_floor((double)(k - 1u) * y);
+  }
+  return fk - fk1 == 1.0 ? hi_c : lo_c;
+}
+
 // `steps` accesses of stochastic rounding at the fixed NVFP4 scale of each
 // segment (x = clamp(w / s, -6, 6), as the Sigma-Delta chain), access k
 // written to bank k.  Element e (row-major within its segment) draws output
 // word e mod 4 of Philox4x32-10 at counter (g lo, g hi, step0 + k, segment
 // index) with g = e / 4, key (k0, k1).
+// TWO_POINT: the two-point chain instead, bank k holding access
+// step0 + k + 1 (no random words).
+template <bool TWO_POINT>
 __global__ __launch_bounds__(kThreads) void k_stochastic_round(const SdArgs args, int steps, int64_t bank_stride,
                                                                uint32_t k0, uint32_t k1, uint32_t step0,
                                                                int seg_base) {
@@ -616,6 +650,13 @@ __global__ __launch_bounds__(kThreads) void k_stochastic_round(const SdArgs args
     for (int u = 0; u < kSdUnroll; ++u) {
       if (cidx[u] >= n) continue;
       uint32_t pk = 0;
+      if (TWO_POINT) {
+        const uint32_t acc = step0 + (uint32_t)k + 1u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pk |= two_point_code(x[u][i], acc) << (4 * i);
+        reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pk;
+        continue;
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {                      // two Philox groups of four elements
         const uint64_t g = (uint64_t)cidx[u] * 2 + h;
@@ -892,7 +933,7 @@ hipError_t launch_harmonize_nvfp4(const fp4q_nv_member* mem, int n, float* share
 }
 
 hipError_t launch_stochastic_round(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride,
-                                   uint64_t seed, uint32_t step0, hipStream_t s) {
+                                   uint64_t seed, uint32_t step0, int two_point, hipStream_t s) {
   for (int base = 0; base < nseg; base += kSdMaxSeg) {
     SdArgs a = {};
     const int cnt = (nseg - base) < kSdMaxSeg ? (nseg - base) : kSdMaxSeg;
@@ -910,8 +951,12 @@ hipError_t launch_stochastic_round(const fp4q_sd_segment* segs, int nseg, int st
       wg += (int32_t)grid_for(a.nchunks[i], (int64_t)kThreads * kSdUnroll);
     }
     a.wg_start[cnt] = wg;
-    hipLaunchKernelGGL(k_stochastic_round, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride,
-                       (uint32_t)seed, (uint32_t)(seed >> 32), step0, base);
+    if (two_point)
+      hipLaunchKernelGGL(k_stochastic_round<true>, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride, 0u, 0u,
+                         step0, base);
+    else
+      hipLaunchKernelGGL(k_stochastic_round<false>, dim3(wg), dim3(kThreads), 0, s, a, steps, bank_stride,
+                         (uint32_t)seed, (uint32_t)(seed >> 32), step0, base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -56,6 +56,7 @@ _SIGS = {
     "fp4q_balance_scale": ([_p, _i, _l, _l, _l, _p, _i, _l, _l, ctypes.c_double, _p, _p, _p], _i),
     "fp4q_sigma_delta_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, _p], _i),
     "fp4q_sigma_delta_schedule": ([ctypes.POINTER(SdSegment), _i, _i, _i, _l, _p], _i),
+    "fp4q_two_point_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, ctypes.c_uint32, _p], _i),
     "fp4q_stochastic_round_requant": ([ctypes.POINTER(SdSegment), _i, _i, _l, ctypes.c_uint64, ctypes.c_uint32,
                                        _p], _i),
     "fp4q_harmonize_nvfp4": ([ctypes.POINTER(NvMember), _i, _p, _p], _i),
@@ -286,6 +287,21 @@ def stochastic_round_requant(segments: Sequence[dict], steps: int, seed: int, st
     _check(lib.fp4q_stochastic_round_requant(arr, len(segments), int(steps), int(bank_stride),
                                              int(seed) & ((1 << 64) - 1), int(step0) & 0xFFFFFFFF, _stream(dev)),
            "stochastic_round_requant")
+
+
+def two_point_requant(segments: Sequence[dict], steps: int, step0: int = 0, bank_stride: int = 0) -> None:
+    """Write ``steps`` banks of the stateless two-point chain (accesses
+    step0 + 1 .. step0 + steps).  Segments as for
+    :func:`sigma_delta_requant`; ``residue`` is not used."""
+    arr = (SdSegment * len(segments))()
+    dev = None
+    for i, s in enumerate(segments):
+        w = s["w"]
+        dev = w.device
+        arr[i] = SdSegment(w.data_ptr(), s["scales"].data_ptr(), s["tensor_scale"].data_ptr(), 0,
+                           s["codes"].data_ptr(), w.shape[0], w.shape[1])
+    _check(lib.fp4q_two_point_requant(arr, len(segments), int(steps), int(bank_stride), int(step0) & 0xFFFFFFFF,
+                                      _stream(dev)), "two_point_requant")
 
 
 # ----------------------------------------------------------------- GEMM ----

@@ -240,6 +240,24 @@ int fp4q_stochastic_round_requant(const fp4q_sd_segment* segs, int nseg, int ste
                                   uint64_t seed, uint32_t step0, void* stream);
 
 /*
+ * Code banks of the stateless two-point chain (F4b) for the looped core.
+ * [LQ] section 2.2 (the bound proof covers the recursive chain, not the
+ * "two-point closed-form difference" of the code-generation benchmark) and
+ * section 4's benchmark; the page gives no formula, and the reading taken:
+ * with the same fixed scale and x = clamp(w / s, -6, 6) as
+ * fp4q_sigma_delta_requant, lo = the largest E2M1 value <= x, hi = the next
+ * one and p = (x - lo) / (hi - lo), access k (k >= 1) takes hi exactly when
+ * floor(k p) - floor((k - 1) p) = 1, else lo (exact; values on the grid are
+ * kept; a zero keeps the sign bit of x; zero-scale blocks give code 0).  No
+ * state: any access is computed directly.  Bank j holds access step0 + j + 1
+ * at segs[i].codes + j * bank_stride_bytes (rules as for
+ * fp4q_stochastic_round_requant); the residue field is not used.
+ * steps in [1, 4096], step0 + steps < 2^24, nseg in [1, 64].
+ */
+int fp4q_two_point_requant(const fp4q_sd_segment* segs, int nseg, int steps, int64_t bank_stride_bytes,
+                           uint32_t step0, void* stream);
+
+/*
  * One member of a fused NVFP4 GEMM (weights quantized separately and
  * concatenated along N).  The ARRAY of members lives in HOST memory; the
  * pointers inside it are device pointers.

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fp4q_sigma_delta_requant", "fp4q_gemm_w4a4", "fp4q_gemm_w4a16", "fp4q_linear_w4a4",
               "fp4q_balance_scale", "fp4q_harmonize_nvfp4", "fp4q_hessian_accumulate",
               "fp4q_macaq_workspace_bytes", "fp4q_macaq_refine", "fp4q_sigma_delta_schedule",
-              "fp4q_stochastic_round_requant", "fp4q_gemm_w4a16_grouped",
+              "fp4q_stochastic_round_requant", "fp4q_gemm_w4a16_grouped", "fp4q_two_point_requant",
               "fp4q_abi_version", "fp4q_status_str",
               "fp4q_last_error"]:
         assert n in names
@@ -101,6 +101,9 @@ def test_validation_happens_before_any_device_work(fp4q):
     assert L.fp4q_stochastic_round_requant(segn, 1, 4, 48, 42, 0, None) == 5
     assert L.fp4q_stochastic_round_requant(segn, 65, 4, 64, 42, 0, None) == 5
     assert L.fp4q_stochastic_round_requant((fp4q.SdSegment * 1)(seg0), 1, 1, 0, 42, 0, None) == 2
+    assert L.fp4q_two_point_requant(segn, 1, 0, 64, 0, None) == 5
+    assert L.fp4q_two_point_requant(segn, 1, 4, 64, (1 << 24) - 3, None) == 5      # step0 + steps >= 2^24
+    assert L.fp4q_two_point_requant(segn, 1, 4, 16, 0, None) == 5
 
 
 def test_harmonize_validation(fp4q):

@@ -468,3 +468,36 @@ def test_stochastic_rounding_looped_core_full_size():
         for k in (0, 1, 17, R - 1):
             bank = got[k, :w.size // 2].reshape(w.shape[0], -1)[rows]
             assert_bytes_equal(bank, packed(want[k]), f"linear {i} access {k}")
+
+
+def test_two_point_chain_bit_exact():
+    # small segments (zero and -0 blocks, tiny values near zero) and the
+    # looped core on sampled rows; banks hold accesses step0 + 1 ..
+    ws = [synth.normal_f32(150 + i, shp, 0.02) for i, shp in enumerate([(24, 64), (8, 128), (7, 32)])]
+    ws[0][5, 16:32] = 0.0
+    ws[1][2, :16] = -0.0
+    ws[1][3, 16:32] *= 1e-9                     # normalised values near zero: tiny
+    ws[1][3, 16] = 0.02                         # values beside one block maximum
+    L = fp4q()
+    segs, stride = _sr_segments(ws, 6)
+    print("two-point chain, 3 segments x 6 accesses", flush=True)
+    L.two_point_requant(segs, 6, step0=3, bank_stride=stride)
+    for i, (s_, w) in enumerate(zip(segs, ws)):
+        st = ONV.tensor_scale_from_amax(np.abs(w).max())
+        want = OSD.two_point_nvfp4(w, range(4, 10), tensor_scale=st)
+        got = host(s_["codes"])
+        for j in range(6):
+            assert_bytes_equal(got[j, :w.size // 2].reshape(w.shape[0], -1), packed(want[4 + j]), f"segment {i} access {4 + j}")
+    wl = synth.looped_sigma_delta(tokens=8)
+    ws = [wl.arrays[f"w{i}"] for i in (0, 4, 12)]
+    segs, stride = _sr_segments(ws, 32)
+    print("two-point chain, looped-core linears x 32 accesses", flush=True)
+    L.two_point_requant(segs, 32, bank_stride=stride)
+    for i, (s_, w) in enumerate(zip(segs, ws)):
+        rows = sample_rows(w.shape[0], k=2, seed=i)
+        st = ONV.tensor_scale_from_amax(np.abs(w).max())
+        want = OSD.two_point_nvfp4(w, (1, 2, 17, 32), rows=rows, tensor_scale=st)
+        got = host(s_["codes"])
+        for k in (1, 2, 17, 32):
+            bank = got[k - 1, :w.size // 2].reshape(w.shape[0], -1)[rows]
+            assert_bytes_equal(bank, packed(want[k]), f"linear {i} access {k}")
