@@ -540,69 +540,102 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
                                                uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-    c0 = hi1 ^ c1 ^ k0;
-    c2 = hi0 ^ c3 ^ k1;
-    c1 = lo1;
-    c3 = lo0;
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;   // one 32x32->64 each
+    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
   return make_uint4(c0, c1, c2, c3);
 }
 
-// Stochastic rounding of x in [-6, 6] to an E2M1 code with one random word:
+// Stochastic rounding of x in [-6, 6] to an E2M1 code with one random word
+// (sr_prepare once per element, sr_pick once per access):
 // lo = the largest E2M1 value <= x, hi = the next one; u = (word >> 8) 2^-24;
-// hi exactly when lo + u (hi - lo) < x, which float64 evaluates exactly
-// (hi - lo is a power of two), so P(hi) = (x - lo) / (hi - lo) up to 2^-24.
-// Values on the grid are kept; a zero value keeps the sign bit of x.
-__device__ __forceinline__ uint32_t sr_code(float x, uint32_t word) {
+// hi exactly when lo + u (hi - lo) < x, so P(hi) = (x - lo) / (hi - lo) up to
+// 2^-24.  Evaluated exactly in integers: with s = 2^24 / (hi - lo) (a power
+// of two), the test is lo s + U < x s for the integer U = word >> 8, and
+// for an integer left side that is lo s + U < ceil(x s); lo s and x s are
+// exact binary32 products below 2^28 in magnitude.  Values on the grid are
+// kept; a zero value keeps the sign bit of x.
+// Bracket of x: lo, the largest E2M1 value <= x, as a code, and whether a
+// next value hi exists; hi's code is lo's plus one (x >= 0) or minus one
+// (x < 0: magnitudes fall towards zero).
+__device__ __forceinline__ uint32_t bracket_lo(float x, bool& has_hi) {
   const float a = __builtin_fabsf(x);
   const uint32_t fl = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
-  const uint32_t ce = fl + (e2m1_decode(fl) < a ? 1u : 0u);       // smallest magnitude >= a
-  uint32_t lo_c, hi_c;
-  bool has_hi;
-  if (__float_as_uint(x) >> 31) {                                 // below: -mag(ce); above: -mag(ce - 1)
-    lo_c = ce | 8u; hi_c = (ce - 1u) | 8u; has_hi = ce > 0u;
-  } else {
-    lo_c = fl; hi_c = fl + 1u; has_hi = fl < 7u;
+  if (__float_as_uint(x) >> 31) {
+    const uint32_t ce = fl + (e2m1_decode(fl) < a ? 1u : 0u);     // smallest magnitude >= a
+    has_hi = ce > 0u;
+    return ce | 8u;
   }
+  has_hi = fl < 7u;
+  return fl;
+}
+__device__ __forceinline__ uint32_t bracket_hi(uint32_t lo_c) { return (lo_c & 8u) ? lo_c - 1u : lo_c + 1u; }
+
+// Per-element state of the stochastic rounding: (C - L) << 4 | code(lo),
+// C - L in [0, 2^24] (0 when x has no upper neighbour).
+__device__ __forceinline__ uint32_t sr_prepare(float x) {
+  bool has_hi;
+  const uint32_t lo_c = bracket_lo(x, has_hi);
   if (!has_hi) return lo_c;
-  const double lo = (double)e2m1_decode(lo_c), hi = (double)e2m1_decode(hi_c);
-  const double t = lo + (double)(word >> 8) * 0x1p-24 * (hi - lo);
-  return t < (double)x ? hi_c : lo_c;
+  const float lo = e2m1_decode(lo_c);
+  // 2^24 / (hi - lo) from the exponent field of hi - lo (0.5, 1 or 2)
+  const float sc = __uint_as_float((278u - (__float_as_uint(e2m1_decode(bracket_hi(lo_c)) - lo) >> 23)) << 23);
+  const int32_t diff = (int32_t)__builtin_ceilf(x * sc) - (int32_t)(lo * sc);
+  return ((uint32_t)diff << 4) | lo_c;
+}
+__device__ __forceinline__ uint32_t sr_pick(uint32_t state, uint32_t word) {
+  const uint32_t lo_c = state & 15u;
+  return (word >> 8) < (state >> 4) ? bracket_hi(lo_c) : lo_c;
 }
 
-// Access k >= 1 of the stateless two-point chain (F4b): lo, hi the E2M1
+// A binary32 y in [0, 1] as m 2^-sh with its 24-bit significand m; sh is
+// clamped to 63, which changes no floor or ceiling below: k m < 2^48.
+__device__ __forceinline__ void split_unit(float y, uint32_t& m, uint32_t& sh) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t e = b >> 23;                                      // y >= 0
+  m = e ? ((b & 0x7FFFFFu) | 0x800000u) : (b & 0x7FFFFFu);
+  const uint32_t s = e ? 150u - e : 149u;
+  sh = s < 63u ? s : 63u;
+}
+
+// Access k >= 1 of the stateless two-point chain (F4b; two_point_prepare
+// once per element, two_point_pick once per access): lo, hi the E2M1
 // neighbours of x, p = (x - lo) / (hi - lo); hi exactly when
-// floor(k p) - floor((k - 1) p) = 1.  Exact in float64 for k < 2^24:
-// x - lo is exact in float32 (lo = 0, or Sterbenz: lo <= x <= 2 lo in
-// magnitude) except on (-0.5, 0), where k p = k + 2 k x; 2 k x and k (x - lo)
-// need at most 49 bits, and hi - lo is a power of two.
-__device__ __forceinline__ uint32_t two_point_code(float x, uint32_t k) {
-  const float a = __builtin_fabsf(x);
-  const uint32_t fl = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
-  const uint32_t ce = fl + (e2m1_decode(fl) < a ? 1u : 0u);
-  uint32_t lo_c, hi_c;
+// floor(k p) - floor((k - 1) p) = 1.  Exact in integers for k < 2^24: x - lo
+// is exact in binary32 (lo = 0, or Sterbenz: lo <= x <= 2 lo in magnitude)
+// and hi - lo is a power of two, so p = m 2^-sh exactly and
+// floor(k p) = (k m) >> sh; on [-0.5, 0), k p = k - k v with v = 2 |x|, so
+// floor(k p) = k - ceil(k v), ceil(k v) = (k m + 2^sh - 1) >> sh.
+// Per-element state of the two-point chain: w0 = m | code(lo) << 24 |
+// neg0 << 28, w1 = sh (m = 0 when x has no upper neighbour or lies on the
+// grid, which makes every access take lo).
+__device__ __forceinline__ void two_point_prepare(float x, uint32_t& w0, uint32_t& w1) {
   bool has_hi;
-  if (__float_as_uint(x) >> 31) {
-    lo_c = ce | 8u; hi_c = (ce - 1u) | 8u; has_hi = ce > 0u;
-  } else {
-    lo_c = fl; hi_c = fl + 1u; has_hi = fl < 7u;
-  }
-  if (!has_hi) return lo_c;
-  double fk, fk1;
-  if (hi_c == 8u) {                                   // x in [-0.5, 0): k p = k + 2 k x
-    fk = (double)k + __builtin_floor(2.0 * (double)k * (double)x);
-    fk1 = (double)(k - 1u) + __builtin_floor(2.0 * (double)(k - 1u) * (double)x);
-  } else {
-    const float lo = e2m1_decode(lo_c), d = e2m1_decode(hi_c) - lo;
-    const double y = (double)(x - lo) / (double)d;    // exact
-    fk = __builtin_floor((double)k * y);
-    fk1 = __builtin_floor((double)(k - 1u) * y);
-  }
-  return fk - fk1 == 1.0 ? hi_c : lo_c;
+  const uint32_t lo_c = bracket_lo(x, has_hi);
+  if (!has_hi) { w0 = lo_c << 24; w1 = 0u; return; }
+  const uint32_t hi_c = bracket_hi(lo_c);
+  const bool neg0 = hi_c == 8u;                       // x in [-0.5, 0)
+  const float lo = e2m1_decode(lo_c);
+  // 1 / (hi - lo) from the exponent field of hi - lo (0.5, 1 or 2): exact
+  const float inv = __uint_as_float((254u - (__float_as_uint(e2m1_decode(hi_c) - lo) >> 23)) << 23);
+  const float y = neg0 ? 2.0f * __builtin_fabsf(x) : (x - lo) * inv;   // v or p, exact
+  uint32_t m, sh;
+  split_unit(y, m, sh);
+  w0 = m | (lo_c << 24) | (neg0 ? 1u << 28 : 0u);
+  w1 = sh;
+}
+__device__ __forceinline__ uint32_t two_point_pick(uint32_t w0, uint32_t w1, uint32_t k) {
+  const uint32_t m = w0 & 0xFFFFFFu, lo_c = (w0 >> 24) & 15u;
+  const bool neg0 = (w0 >> 28) & 1u;
+  const uint64_t prod = (uint64_t)k * m, prev = prod - m;          // k m and (k - 1) m
+  const uint64_t bias = neg0 ? (uint64_t(1) << w1) - 1u : 0u;      // ceiling instead of floor
+  const uint64_t d = ((prod + bias) >> w1) - ((prev + bias) >> w1);
+  return (neg0 ? d == 0u : d == 1u) ? bracket_hi(lo_c) : lo_c;
 }
 
 // `steps` accesses of stochastic rounding at the fixed NVFP4 scale of each
@@ -645,6 +678,15 @@ __global__ __launch_bounds__(kThreads) void k_stochastic_round(const SdArgs args
   }
   uint8_t* codes = args.codes[seg];
   const uint32_t sid = (uint32_t)(seg_base + seg);
+  // per-element state, computed once for all accesses
+  uint32_t w0[kSdUnroll][8], w1[kSdUnroll][8];
+#pragma unroll
+  for (int u = 0; u < kSdUnroll; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (TWO_POINT) two_point_prepare(x[u][i], w0[u][i], w1[u][i]);
+      else w0[u][i] = sr_prepare(x[u][i]);
+    }
   for (int k = 0; k < steps; ++k) {
 #pragma unroll
     for (int u = 0; u < kSdUnroll; ++u) {
@@ -653,18 +695,17 @@ __global__ __launch_bounds__(kThreads) void k_stochastic_round(const SdArgs args
       if (TWO_POINT) {
         const uint32_t acc = step0 + (uint32_t)k + 1u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pk |= two_point_code(x[u][i], acc) << (4 * i);
-        reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pk;
-        continue;
-      }
+        for (int i = 0; i < 8; ++i) pk |= two_point_pick(w0[u][i], w1[u][i], acc) << (4 * i);
+      } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {                      // two Philox groups of four elements
-        const uint64_t g = (uint64_t)cidx[u] * 2 + h;
-        const uint4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), step0 + (uint32_t)k, sid, k0, k1);
-        pk |= sr_code(x[u][4 * h + 0], r.x) << (16 * h);
-        pk |= sr_code(x[u][4 * h + 1], r.y) << (16 * h + 4);
-        pk |= sr_code(x[u][4 * h + 2], r.z) << (16 * h + 8);
-        pk |= sr_code(x[u][4 * h + 3], r.w) << (16 * h + 12);
+        for (int h = 0; h < 2; ++h) {                    // two Philox groups of four elements
+          const uint64_t g = (uint64_t)cidx[u] * 2 + h;
+          const uint4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), step0 + (uint32_t)k, sid, k0, k1);
+          pk |= sr_pick(w0[u][4 * h + 0], r.x) << (16 * h);
+          pk |= sr_pick(w0[u][4 * h + 1], r.y) << (16 * h + 4);
+          pk |= sr_pick(w0[u][4 * h + 2], r.z) << (16 * h + 8);
+          pk |= sr_pick(w0[u][4 * h + 3], r.w) << (16 * h + 12);
+        }
       }
       reinterpret_cast<uint32_t*>(codes + (int64_t)k * bank_stride)[cidx[u]] = pk;
     }
