@@ -225,7 +225,7 @@ int fp4q_sigma_delta_schedule(const fp4q_sd_segment* segs, int nseg, int n_rtn, 
  * scale and x = clamp(w / s, -6, 6) as fp4q_sigma_delta_requant; per
  * element, lo = the largest E2M1 value <= x, hi = the next one,
  * u = (word >> 8) * 2^-24: the code is hi exactly when lo + u (hi - lo) < x
- * (exact in float64), so P(hi) = (x - lo) / (hi - lo) up to 2^-24; values
+ * (decided exactly, in integers), so P(hi) = (x - lo) / (hi - lo) up to 2^-24; values
  * on the grid are kept; a zero value keeps the sign bit of x; zero-scale
  * blocks give code 0.
  * Random words: Philox4x32-10 (Salmon et al., SC'11) with key
