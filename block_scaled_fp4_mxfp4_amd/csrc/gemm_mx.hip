@@ -672,7 +672,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3_grouped(const MxGrou
 #endif
 #ifndef FP4Q_NV_BN
 #if FP4Q_NV_M32
-#define FP4Q_NV_BN 128
+#define FP4Q_NV_BN 128        // narrow tiles (two workgroups per CU); 320-wide ones are picked by shape
 #else
 #define FP4Q_NV_BN 160
 #endif
@@ -810,6 +810,19 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a
   if (K % (2 * FP4Q_NV_CB) || M * (K / 2) >= (int64_t(1) << 32) || N * (K / 2) >= (int64_t(1) << 32))
     return launch_gemm_nvfp4_staged(a, as, ats, b, bs, bts, M, N, K, y, ldy, s);
   MxArgs p{a, as, b, bs, ats, bts, M, N, K, y, ldy, 0, 0};
+#if FP4Q_NV_M32
+  // Tile width by rounds: 128-wide tiles run two workgroups per CU, 320-wide
+  // ones one (LDS); a round of either keeps a CU busy for about the same
+  // width x workgroups, so the cost is rounds x that product, and the width
+  // with the smaller cost wins (ties: 128).  4096 x 10240: 128 -> 1280 tiles,
+  // 2.5 rounds of 512; 320 -> 512 tiles, exactly 2 rounds of 256 (7% faster).
+  if constexpr (FP4Q_NV_BN == 128 && FP4Q_NV_BM == 256) {
+    const int64_t cus = device_cus(), tm = cdiv_i(M, 256);
+    const int64_t c128 = cdiv_i(tm * cdiv_i(N, 128), 2 * cus) * 256;
+    const int64_t c320 = cdiv_i(tm * cdiv_i(N, 320), cus) * 320;
+    if (c320 < c128) return launch_mx3<FMT_NV, 256, 320, FP4Q_NV_CB, 1, FP4Q_NV_NW, FP4Q_NV_NS, 1>(p, s);
+  }
+#endif
   return launch_mx3<FMT_NV, FP4Q_NV_BM, FP4Q_NV_BN, FP4Q_NV_CB, 1, FP4Q_NV_NW, FP4Q_NV_NS, FP4Q_NV_M32>(p, s);
 }
 

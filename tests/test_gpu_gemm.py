@@ -53,6 +53,22 @@ def test_nvfp4_tiny_config():
     _check(y, OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), "nvfp4 tiny config")
 
 
+def test_nvfp4_gemm_wide_tiles_ragged():
+    # 4000 x 10100 takes the 320-wide tiles (two full rounds) with partial
+    # tiles in both M and N; sampled rows include the last ones
+    L = fp4q()
+    x = synth.heavy_tailed_f32(210, 211, (4000, 256))
+    w = synth.normal_f32(212, (10100, 256), 0.02)
+    ac, as_, at = _nv_gpu(dev_f32(x))
+    bc, bs, bt = _nv_gpu(dev_f32(w))
+    y = host(L.gemm_w4a4(L.NVFP4, ac, as_, at, bc, bs, bt))
+    rows, cols = sample_rows(4000, 40, 3), sample_rows(10100, 400, 4)
+    cx, sx, tx = ONV.quantize(x)
+    cw, sw, tw = ONV.quantize(w)
+    ref = OG.w4a4_nvfp4(cx[rows], sx[rows], tx, cw[cols], sw[cols], tw)
+    _check(y[np.ix_(rows, cols)], ref, "nvfp4 4000x10100x256 (320-wide tiles)")
+
+
 def test_nvfp4_prefill_full_size_sampled():
     wl = synth.nvfp4_prefill()
     xb, wb = wl.arrays["x_bf16"], wl.arrays["w_bf16"]
