@@ -155,7 +155,7 @@ def main():
 
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK["fp16_TFLOPs"],
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK["fp16_TFLOPs"], 4), "traffic": traffic,
-                "kernel": "k_gemm_mx3<FMT_NV, 256, 128, 64, 1, 8, 2, M32 = 1> (8 wavefronts, LDS-DMA tiles, exact NVFP4 dequant, 32x32x16 fp16 MFMA)",
+                "kernel": "k_gemm_mx3<FMT_NV, 256, 320, 64, 1, 8, 2, M32 = 1> (8 wavefronts, 256x320 tiles, LDS-DMA tiles, exact NVFP4 dequant, 32x32x16 fp16 MFMA)",
                 "algorithmic": "2*M*N*K flop per launch (M=4096, N=10240, K=5120)",
                 "frac_of_fp4_peak": round(gemm_tflops / PEAK["fp4_TFLOPs"], 4)}
 
