@@ -178,6 +178,16 @@ def main():
     }
 
     if not args.only_step and not args.no_extras:
+        # context, not part of the path: the platform's dense fp16 GEMM
+        # (hipBLASLt through torch.mm) on the same shape and operand layout
+        log("context: library fp16 GEMM on the same shape")
+        a16, w16 = x.to(torch.float16), w.to(torch.float16)
+        y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+        tl = _time_op(torch, stream, lambda i: torch.mm(a16, w16.t(), out=y16), 20)
+        out["context_library_fp16_gemm"] = {
+            **_fl(tl, flops, "fp16_TFLOPs"), "op": "torch.mm(fp16 X, fp16 W^T) -> fp16, hipBLASLt",
+            "shape": [M, N, K], "ours_gemm_TFLOPs": round(gemm_tflops, 2)}
+        del a16, w16, y16
         out["extras"] = run_extras(L, synth, np, torch, dev, stream, log)
 
     if not args.only_step and not args.no_cpu_baseline:

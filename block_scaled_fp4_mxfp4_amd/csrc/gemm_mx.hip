@@ -98,6 +98,19 @@ __device__ __forceinline__ v8h dequant8(uint32_t w, v2h sb) {
   return __builtin_bit_cast(v8h, uint4{o0, o1, o2, o3});
 }
 
+// Two of the eight values of dequant8 (dword q of its result), for
+// splitting one fragment's dequantization across several instructions.
+__device__ __forceinline__ uint32_t dequant2(uint32_t w, v2h sb, int q) {
+  v2h t;
+  switch (q) {
+    case 0: t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)); break;
+    case 1: t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)); break;
+    case 2: t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)); break;
+    default: t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)); break;
+  }
+  return __builtin_bit_cast(uint32_t, t * sb);
+}
+
 // vmcnt(n) for a wave-uniform n in [0, 31] (the count must be an immediate)
 __device__ __forceinline__ void wait_vm(int n) {
 #define FP4Q_VMW(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
@@ -476,6 +489,7 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+          if (ks | t) __builtin_amdgcn_sched_barrier(0);
           v8h ha[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
@@ -483,14 +497,38 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
             ha[i] = dequant8(w, sa[i][t >> 1]);
           }
           __builtin_amdgcn_s_setprio(1);
+          // B fragment j + 1 is dequantized in FM parts, one after each
+          // multiply of fragment j, into the other of two register sets; the
+          // scheduling groups below keep that one-multiply, few-VALU rhythm
+          // (measured 1% faster than dequantizing each fragment whole
+          // before its multiplies; results bit-identical)
+          uint32_t hb[2][4];
+          {
+            const uint32_t w = t == 0 ? qb[0].x : t == 1 ? qb[0].y : t == 2 ? qb[0].z : qb[0].w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hb[0][q] = dequant2(w, sb[0][t >> 1], q);
+          }
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const uint32_t w = t == 0 ? qb[j].x : t == 1 ? qb[j].y : t == 2 ? qb[j].z : qb[j].w;
-            const v8h hb = dequant8(w, sb[j][t >> 1]);
+            const v8h cur = __builtin_bit_cast(v8h, uint4{hb[j & 1][0], hb[j & 1][1], hb[j & 1][2], hb[j & 1][3]});
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], hb, acc[i][j], 0, 0, 0);
+            for (int i = 0; i < FM; ++i) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[i], cur, acc[i][j], 0, 0, 0);
+              if (j + 1 < FN) {
+                const int jn = j + 1 < FN ? j + 1 : j;
+                const uint32_t w = t == 0 ? qb[jn].x : t == 1 ? qb[jn].y : t == 2 ? qb[jn].z : qb[jn].w;
+#pragma unroll
+                for (int q = i * 4 / FM; q < (i + 1) * 4 / FM; ++q) hb[(j + 1) & 1][q] = dequant2(w, sb[jn][t >> 1], q);
+              }
+            }
           }
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one matrix instruction
+              if (j + 1 < FN) __builtin_amdgcn_sched_group_barrier(0x002, 8 / FM, 0);   // then VALU
+            }
           __builtin_amdgcn_s_setprio(0);
         }
       }
