@@ -25,6 +25,8 @@
 // form reads it from a separate amax pass.
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "codec.h"
@@ -814,8 +816,12 @@ hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8
     int64_t grid = groups < n_cu ? groups : n_cu;
     const int64_t rpw = (N + grid - 1) / grid;
     grid = (N + rpw - 1) / rpw;
-    // allow the full 160 KiB of LDS once per process
-    static hipError_t attr = [] {
+    // allow the full 160 KiB of LDS, once per device (the attribute is set
+    // with that device current)
+    static std::atomic<int> attr_set[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
       const void* ks[3] = {reinterpret_cast<const void*>(&k_decode_stream<false, 1>),
                            reinterpret_cast<const void*>(&k_decode_stream<true, 5>),
                            reinterpret_cast<const void*>(&k_decode_stream<true, 10>)};
@@ -823,9 +829,8 @@ hipError_t launch_gemm_nvfp4_skinny(const void* a_bf16, int64_t lda, const uint8
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
       }
-      return hipSuccess;
-    }();
-    if (attr != hipSuccess) return attr;
+      attr_set[dev].store(1, std::memory_order_release);
+    }
     auto launch = [&](auto kern) -> hipError_t {
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kStThreads), (size_t)L.total, s,
                          reinterpret_cast<const uint16_t*>(a_bf16), lda, a_codes, a_scales, ats,
