@@ -286,3 +286,23 @@ def test_w4a16_grouped_equals_single_launches():
     cw, sw, tw = ONV.quantize(w)
     ref = OG.matmul_nt(OF.bf16_bits_to_f32(xb).astype(np.float64), ONV.dequantize(cw, sw, tw))
     _check(got[-3], ref, "grouped W4A16 130x200x384")
+
+
+def test_w4a16_grouped_spans_several_launches():
+    # 37 problems: more than one grouped launch holds (16 per launch), with
+    # mixed K (launch order is longest K first) and ragged M, N
+    L = fp4q()
+    rng = np.random.default_rng(950)
+    probs = []
+    for i in range(37):
+        M = int(rng.integers(1, 300))
+        N = int(rng.integers(1, 20)) * 32 + int(rng.integers(0, 2)) * 7
+        K = int(rng.choice([128, 256, 384, 768, 1024]))
+        a = dev_bf16(synth.f32_to_bf16_bits(synth.heavy_tailed_f32(960 + i, 961, (M, K))))
+        c, sc, ts = L.quantize_nvfp4(dev_f32(synth.normal_f32(962 + i, (N, K), 0.02)))
+        probs.append((a, c, sc, ts))
+    print(f"grouped W4A16: {len(probs)} problems in {(len(probs) + 15) // 16} launches", flush=True)
+    got = [host(y) for y in L.gemm_w4a16_grouped(probs)]
+    for i, pr in enumerate(probs):
+        want = host(L.gemm_w4a16(*pr))
+        assert np.array_equal(got[i].view(np.uint32), want.view(np.uint32)), f"problem {i}"
