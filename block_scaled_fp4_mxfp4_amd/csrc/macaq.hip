@@ -272,6 +272,11 @@ __global__ __launch_bounds__(kThreads) void k_grad(const float* __restrict__ w, 
 // is).  A 32-block is 32 consecutive threads, so its all-zero flag is one
 // ballot.
 
+// log2 |grid[gi - 1] - grid[gi]| + 1 in bits 2 gi, 2 gi + 1 for gi = 1..14
+// (steps 2, 1, 1, then eight of 0.5, then 1, 1, 2); the step up from gi is
+// the step down from gi + 1
+constexpr uint32_t kStepLog2 = 0x25000058u;
+
 __device__ __forceinline__ bool better(double g, int f, double bg, int bf) {
   return g > bg || (g == bg && f < bf);
 }
@@ -321,17 +326,21 @@ __global__ __launch_bounds__(NT) void k_flip(const float* __restrict__ w, int64_
     for (int u = 0; u < U; ++u) {
       if (!(st[u] & (1u << 12))) continue;
       const int64_t j = tid + (int64_t)NT * u;
+      // d = (grid[gi -+ 1] - grid[gi]) * 2^e is a signed power of two,
+      // 2^(e + l), with l = log2 of the grid step (kStepLog2), so 2d and
+      // d * d are built from the exponent; the gain is then the same
+      // rounded expression (2d) g - (d d) hd as with d formed by subtraction
       const int gi = (int)(st[u] & 15u);
-      const double s = pow2d((int32_t)((st[u] >> 4) & 0xFFu) - 127), v = grid_value(gi);
+      const int e = (int)((st[u] >> 4) & 0xFFu) - 127;
       if (gi > 0) {
-        const double d = (grid_value(gi - 1) - v) * s;
-        const double gain = (2.0 * d) * g[u] - (d * d) * hd[u];
-        if (gain > bg) { bg = gain; bf = (int)(2 * j); bd = d; }
+        const int a = e + (int)((kStepLog2 >> (2 * gi)) & 3u) - 1;          // d = -2^a
+        const double gain = (-pow2d(a + 1)) * g[u] - pow2d(2 * a) * hd[u];
+        if (gain > bg) { bg = gain; bf = (int)(2 * j); bd = -pow2d(a); }
       }
       if (gi < 14) {
-        const double d = (grid_value(gi + 1) - v) * s;
-        const double gain = (2.0 * d) * g[u] - (d * d) * hd[u];
-        if (gain > bg) { bg = gain; bf = (int)(2 * j + 1); bd = d; }
+        const int a = e + (int)((kStepLog2 >> (2 * (gi + 1))) & 3u) - 1;    // d = +2^a
+        const double gain = pow2d(a + 1) * g[u] - pow2d(2 * a) * hd[u];
+        if (gain > bg) { bg = gain; bf = (int)(2 * j + 1); bd = pow2d(a); }
       }
     }
 #pragma unroll
