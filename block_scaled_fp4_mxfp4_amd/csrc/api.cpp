@@ -106,6 +106,16 @@ int quantize_nvfp4_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, 
   if (!aligned16(codes)) return fail(FP4Q_ERR_BAD_ALIGN, "codes not 16-byte aligned");
   if (!(reinterpret_cast<uintptr_t>(tensor_scale) % 4 == 0)) return fail(FP4Q_ERR_BAD_ALIGN, "tensor_scale not 4-byte aligned");
   if (tensor_scale_is_input != 0 && tensor_scale_is_input != 1) return fail(FP4Q_ERR_BAD_ARG, "tensor_scale_is_input must be 0 or 1");
+  // with a computed tensor scale the scales buffer first holds 32-bit
+  // partial maxima
+  if (!tensor_scale_is_input && (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return fail(FP4Q_ERR_BAD_ALIGN, "scales must be 4-byte aligned when the tensor scale is computed");
+  // every workgroup reads the tensor-scale cell while others write scales
+  {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(scales), hi = lo + (uintptr_t)(rows * (cols / 16));
+    const uintptr_t c = reinterpret_cast<uintptr_t>(tensor_scale);
+    if (c + sizeof(float) > lo && c < hi) return fail(FP4Q_ERR_BAD_ARG, "tensor_scale lies inside the scales buffer");
+  }
   if (int st = check_device()) return st;
   return launch_status(fp4q::launch_quant_nvfp4(x, x_dtype == FP4Q_BF16, rows, cols, ldx, codes, scales,
                                                 tensor_scale, tensor_scale_is_input, four_six,
@@ -339,7 +349,7 @@ int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, con
   if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return fail(FP4Q_ERR_NULL_PTR, "operand pointer is NULL");
   if (fmt == FP4Q_NVFP4 && (!a_tscale || !b_tscale)) return fail(FP4Q_ERR_NULL_PTR, "NVFP4 needs both tensor scales");
   if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_BAD_SHAPE, "M, N and K must be > 0");
-  if (K % 128) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 128");
+  if (K % 32) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 32");
   if ((reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales)) & 7u)
     return fail(FP4Q_ERR_BAD_ALIGN, "scales must be 8-byte aligned");
   if (ldy < N) return fail(FP4Q_ERR_BAD_SHAPE, "ldy < N");
@@ -364,7 +374,7 @@ int check_w4a16(const void* a_bf16, int64_t lda, const uint8_t* b_codes, const u
                 const float* b_tscale, int64_t M, int64_t N, int64_t K, const float* y, int64_t ldy) {
   if (!a_bf16 || !b_codes || !b_scales || !b_tscale || !y) return fail(FP4Q_ERR_NULL_PTR, "operand pointer is NULL");
   if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_BAD_SHAPE, "M, N and K must be > 0");
-  if (K % 128) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 128");
+  if (K % 32) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 32");
   if (lda < K || ldy < N) return fail(FP4Q_ERR_BAD_SHAPE, "lda < K or ldy < N");
   if (reinterpret_cast<uintptr_t>(b_scales) & 7u) return fail(FP4Q_ERR_BAD_ALIGN, "b_scales must be 8-byte aligned");
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return fail(FP4Q_ERR_BAD_SHAPE, "size too large");
@@ -408,7 +418,7 @@ int fp4q_linear_w4a4(const void* a_bf16, int64_t lda, float* a_tscale, int a_tsc
   if (!a_bf16 || !a_tscale || !b_codes || !b_scales || !b_tscale || !y) return fail(FP4Q_ERR_NULL_PTR, "operand pointer is NULL");
   if (M < 1 || M > 16) return fail(FP4Q_ERR_BAD_SHAPE, "M must be in [1, 16]");
   if (N <= 0 || K <= 0) return fail(FP4Q_ERR_BAD_SHAPE, "N and K must be > 0");
-  if (K % 128) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 128");
+  if (K % 32) return fail(FP4Q_ERR_BAD_SHAPE, "K must be a multiple of 32");
   if (!fp4q::skinny_supported(K)) return fail(FP4Q_ERR_BAD_SHAPE, "K too large for the fused decode kernel (max 7168)");
   if (lda < K || ldy < N) return fail(FP4Q_ERR_BAD_SHAPE, "lda < K or ldy < N");
   if (reinterpret_cast<uintptr_t>(b_scales) & 7u) return fail(FP4Q_ERR_BAD_ALIGN, "b_scales must be 8-byte aligned");

@@ -163,6 +163,20 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in_g / gsz;
 }
 
+// Up to four scale bytes of one row from src (nullptr: none), little
+// endian; bytes at or past the row end (`left` bytes remain in the row) are
+// zero, so a K tail whose codes are zero also has zero scales: a stray
+// E4M3 NaN byte of the next row would turn 0 x scale into NaN.
+__device__ __forceinline__ uint32_t scale_word(const uint8_t* src, int64_t left, bool words) {
+  if (!src) return 0u;
+  if (words && left >= 4) return *reinterpret_cast<const uint32_t*>(src);
+  uint32_t v = 0u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (b < left) v |= (uint32_t)src[b] << (8 * b);
+  return v;
+}
+
 template <int FMT, int BM, int BN, int MINB>
 __global__ __launch_bounds__(kThreads, MINB) void k_gemm(const GemmArgs p) {
   using T = FmtTraits<FMT>;
@@ -189,7 +203,10 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(const GemmArgs p) {
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t ldb = p.K / 2, lds = p.K / (FMT == FMT_MX ? 32 : 16);
-  const int KT = (int)((p.K + BK - 1) / BK);   // the last stage may be half empty (K % BK == 128)
+  const int KT = (int)((p.K + BK - 1) / BK);   // the last stage may be partly empty (K % 32 == 0 only)
+  // scale rows are whole 4-byte words when K / 32 (MXFP4) or K / 16 is a
+  // multiple of 4; otherwise they are read byte by byte
+  const bool words = (lds & 3) == 0;
 
   uint4 ra[A_LD], rb[B_LD];
   uint32_t rs[SC_LD];
@@ -224,15 +241,15 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(const GemmArgs p) {
       const int c = tid + kThreads * i;            // (row, word) of the staged scales
       const int row = c / SCW, w = c % SCW;
       const int64_t kb = (int64_t)kt * SCB + 4 * w;
-      uint32_t v = 0u;
+      const uint8_t* src = nullptr;
       if (row < A_SC) {
         const int64_t r = m0 + row;
-        if (r < p.M && kb < lds) v = *reinterpret_cast<const uint32_t*>(p.As + r * lds + kb);
+        if (r < p.M && kb < lds) src = p.As + r * lds + kb;
       } else if (row < SC_ROWS) {
         const int64_t r = n0 + (row - A_SC);
-        if (r < p.N && kb < lds) v = *reinterpret_cast<const uint32_t*>(p.Bs + r * lds + kb);
+        if (r < p.N && kb < lds) src = p.Bs + r * lds + kb;
       }
-      rs[i] = v;
+      rs[i] = scale_word(src, lds - kb, words);
     }
   };
   auto sstore = [&](int buf) {

@@ -105,7 +105,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int rg = wave & 1, kh = wave >> 1;            // row group, K half
-  const int KT = (int)(K / 128);
+  // K stages of 128; with K % 128 != 0 the last one is partly empty: lane
+  // group g of stage kt holds 32-element block 4 kt + g, present while it is
+  // below K / 32, and absent blocks contribute zero codes and zero scales
+  const int KT = (int)((K + 127) / 128), nblk = (int)(K / 32);
   const int kt_begin = kh ? KT / 2 : 0, kt_end = kh ? KT : KT / 2;
 
   // weight rows of this lane (one per fragment), clamped into the tensor
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(
       const int kt = kt0 + p;
 #pragma unroll
       for (int f = 0; f < FRAGS; ++f) {
-        if (kt < kt_end) {
+        if (kt < kt_end && 4 * kt + g < nblk) {
           const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(brow[f] + (int64_t)kt * 64));
           st.q[p][f] = uint4{q[0], q[1], q[2], q[3]};
           st.s[p][f] = *reinterpret_cast<const uint16_t*>(bsrow[f] + (int64_t)kt * 8);
@@ -231,8 +234,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(
       const int kt = kt0 + p;
       if (kt < kt_end) {
         // A: lane group g owns elements [32 g, 32 g + 32) of the stage
-        const uint4 qa = *reinterpret_cast<const uint4*>(lAc + r16 * lrow + (int64_t)kt * 64 + g * 16);
-        const uint32_t wsa = *reinterpret_cast<const uint16_t*>(lAs + r16 * lsrow + (int64_t)kt * 8 + 2 * g);
+        const bool va = 4 * kt + g < nblk;
+        const uint4 qa = va ? *reinterpret_cast<const uint4*>(lAc + r16 * lrow + (int64_t)kt * 64 + g * 16)
+                            : uint4{0u, 0u, 0u, 0u};
+        const uint32_t wsa = va ? *reinterpret_cast<const uint16_t*>(lAs + r16 * lsrow + (int64_t)kt * 8 + 2 * g) : 0u;
         v2h sa0, sa1;
         e4m3x2_to_h2(wsa, sa0, sa1);
         v2h sb[FRAGS][2];

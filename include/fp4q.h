@@ -87,11 +87,14 @@ const char* fp4q_last_error(void);
  * scales:  [rows][cols/16] E4M3 bytes (output).  With
  *          tensor_scale_is_input == 0 the call first uses this buffer as
  *          scratch for per-workgroup partial maxima (no allocation), then
- *          overwrites it with the block scales.
+ *          overwrites it with the block scales; it must then be 4-byte
+ *          aligned (FP4Q_ERR_BAD_ALIGN).
  * tensor_scale: one fp32.  tensor_scale_is_input == 0: the library computes
  *          A over the whole tensor on the stream and writes s_t here (the
  *          location is also used as the reduction cell while the call runs);
- *          == 1: s_t is read from here (must be finite and >= +0).
+ *          == 1: s_t is read from here (must be finite and >= +0).  In
+ *          both modes the cell must not lie inside the scales buffer
+ *          (FP4Q_ERR_BAD_ARG).
  */
 int fp4q_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                         uint8_t* codes, uint8_t* scales, float* tensor_scale,
@@ -353,7 +356,9 @@ int fp4q_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const d
  * fmt == FP4Q_NVFP4: a_scales [M][K/16], b_scales [N][K/16] E4M3;
  *                    a_tscale, b_tscale point to one fp32 each.
  * a_codes [M][K/2], b_codes [N][K/2] (16-byte aligned); scales 8-byte
- * aligned; K a multiple of 128; y [M][ldy] fp32 (4-byte aligned), ldy >= N.
+ * aligned; K a multiple of 32 (one MXFP4 block; [MQ] MXFP4 box);
+ * y [M][ldy] fp32 (4-byte aligned), ldy >= N.  Shapes with K % 128 != 0
+ * run on register-staged kernels that zero the partial last K stage.
  */
 int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
@@ -364,7 +369,7 @@ int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, con
  * The matrix product the looped core runs on each step's re-quantized weight
  * ([LQ] section 4: the core-linear microbenchmark with online NVFP4 codes).
  * a: [M][lda] bf16, 16-byte aligned, lda % 8 == 0.  B as for NVFP4 above.
- * K a multiple of 128.
+ * K a multiple of 32.
  */
 int fp4q_gemm_w4a16(const void* a_bf16, int64_t lda,
                     const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
@@ -404,7 +409,7 @@ int fp4q_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, void* stream
  * NVFP4 activation-quantization kernel).  Quantizes A (bf16) exactly as
  * fp4q_quantize_nvfp4 does and multiplies by the NVFP4 weight B;
  * Y is bit-identical to fp4q_quantize_nvfp4 followed by fp4q_gemm_w4a4.
- * M in [1, 16]; K a multiple of 128 and at most 7168 (A is held on chip).
+ * M in [1, 16]; K a multiple of 32 and at most 7168 (A is held on chip).
  * a_tscale: one fp32, same in/out rule as fp4q_quantize_nvfp4's
  * tensor_scale (with a_tscale_is_input == 0 every workgroup derives s_t
  * from the exact amax of A, so s_t equals fp4q_quantize_nvfp4's).

@@ -65,7 +65,23 @@ def test_validation_happens_before_any_device_work(fp4q):
     assert L.fp4q_quantize_mxfp4(fake16, 1, 4, 64, 64, None, 3, fake16, fake, None) == 5
     assert L.fp4q_gemm_w4a4(5, fake16, fake16, fake, fake16, fake16, fake, 4, 4, 128, fake16, 4, None) == 4
     assert L.fp4q_gemm_w4a4(0, fake16, fake16, None, fake16, fake16, fake, 4, 4, 128, fake16, 4, None) == 1
-    assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, 4, 4, 96, fake16, 4, None) == 2
+    # K must be a multiple of 32 (one MXFP4 block): 48 is refused, 96 passes
+    # validation and only then meets the device check
+    assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, 4, 4, 48, fake16, 4, None) == 2
+    assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, 4, 4, 96, fake16, 4, None) == 6
+    assert L.fp4q_gemm_w4a16(fake16, 96, fake16, fake16, fake, 4, 4, 80, fake16, 4, None) == 2
+    assert L.fp4q_gemm_w4a16(fake16, 96, fake16, fake16, fake, 4, 4, 96, fake16, 4, None) == 6
+    assert L.fp4q_linear_w4a4(fake16, 160, fake, 0, fake16, fake16, fake, 2, 8, 144, fake16, 8, None) == 2
+    assert L.fp4q_linear_w4a4(fake16, 160, fake, 0, fake16, fake16, fake, 2, 8, 160, fake16, 8, None) == 6
+    # a computed tensor scale uses the scales buffer for 32-bit partial
+    # maxima: it must be 4-byte aligned (a given tensor scale does not need it)
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, P(0x1001), P(0x2000), 0, None) == 3
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, P(0x1001), P(0x2000), 1, None) == 6
+    # the tensor-scale cell must not lie inside the scales (4 rows x 2 bytes)
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, P(0x1000), P(0x1004), 0, None) == 5
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, P(0x1000), P(0x1004), 1, None) == 5
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, P(0x1002), P(0x1000), 1, None) == 5   # straddles the start
+    assert L.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, P(0x1000), P(0x1008), 1, None) == 6
     assert L.fp4q_gemm_w4a4(1, fake16, fake16, None, fake16, fake16, None, 4, 8, 128, fake16, 4, None) == 2
     assert L.fp4q_linear_w4a4(fake16, 128, fake, 0, fake16, fake16, fake, 17, 8, 128, fake16, 8, None) == 2
     assert L.fp4q_linear_w4a4(fake16, 8192, fake, 0, fake16, fake16, fake, 1, 8, 8192, fake16, 8, None) == 2
@@ -132,7 +148,7 @@ def test_device_check_without_gpu(fp4q):
     if torch.cuda.is_available():
         pytest.skip("host has a GPU")
     fake16 = ctypes.c_void_p(0x10000)
-    st = fp4q.lib.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, fake16, fake16, 0, None)
+    st = fp4q.lib.fp4q_quantize_nvfp4(fake16, 1, 4, 32, 32, fake16, fake16, ctypes.c_void_p(0x20000), 0, None)
     assert st == 6
 
 

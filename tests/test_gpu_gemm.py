@@ -116,6 +116,41 @@ def test_mxfp4_gemm_both_column_tiles(M, N, K):
     _check(y[np.ix_(rows, cols)], OG.w4a4_mxfp4(cx, sx, cw, sw), f"mxfp4 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(768, 22400, 128), (600, 25000, 384), (1000, 30000, 256), (300, 9000, 1152)])
+def test_mxfp4_gemm_many_tiles_ragged(M, N, K):
+    # more output tiles than compute units, partial tiles in M and N, and K
+    # that is (1000 x 30000 x 256) or is not (K = 128, 384, 1152) a whole
+    # number of the direct-load kernel's 256-element stages
+    x = synth.heavy_tailed_f32(230 + M, 231, (M, K))
+    w = synth.normal_f32(232 + K, (N, K), 0.02)
+    L = fp4q()
+    ac, as_ = L.quantize_mxfp4(dev_f32(x), None, True)
+    bc, bs = L.quantize_mxfp4(dev_f32(w), None, True)
+    y = host(L.gemm_w4a4(L.MXFP4, ac, as_, None, bc, bs, None))
+    assert np.isfinite(y).all()
+    rows, cols = sample_rows(M, 40, 7), sample_rows(N, 300, 8)
+    cx, sx = OMX.quantize(OMX.hadamard32_scale(x[rows]))
+    cw, sw = OMX.quantize(OMX.hadamard32_scale(w[cols]))
+    _check(y[np.ix_(rows, cols)], OG.w4a4_mxfp4(cx, sx, cw, sw), f"mxfp4 {M}x{N}x{K} (many tiles)")
+
+
+def test_mxfp4_gemm_strided_output():
+    # ldy > N with ldy % 4 != 0: the output leaves through the masked path
+    L = fp4q()
+    M, N, K, ldy = 300, 500, 256, 503
+    x = synth.heavy_tailed_f32(240, 241, (M, K))
+    w = synth.normal_f32(242, (N, K), 0.02)
+    ac, as_ = L.quantize_mxfp4(dev_f32(x), None, True)
+    bc, bs = L.quantize_mxfp4(dev_f32(w), None, True)
+    yb = torch.full((M, ldy), 7.0, dtype=torch.float32, device="cuda:0")
+    L.gemm_w4a4(L.MXFP4, ac, as_, None, bc, bs, None, out=yb[:, :N])
+    y = host(yb)
+    assert (y[:, N:] == 7.0).all(), "columns past N were written"
+    cx, sx = OMX.quantize(OMX.hadamard32_scale(x))
+    cw, sw = OMX.quantize(OMX.hadamard32_scale(w))
+    _check(y[:, :N], OG.w4a4_mxfp4(cx, sx, cw, sw), "mxfp4 300x500x256 ldy 503")
+
+
 def test_mxfp4_transform_full_size_sampled():
     wl = synth.mxfp4_transform()
     xb, wb = wl.arrays["x_bf16"], wl.arrays["w_bf16"]
@@ -210,6 +245,45 @@ def test_decode_ragged(N, K):
         assert_bytes_equal(host(yf).view(np.uint32), host(yu).view(np.uint32), f"fused vs unfused N={N} K={K} M={M}")
         cx, sx, tx = ONV.quantize(OF.bf16_bits_to_f32(xb[:M]))
         _check(host(yf), OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), f"decode N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("K", [32, 96, 160, 4128])
+def test_gemm_k_multiple_of_32(K):
+    # K needs only to be a multiple of 32 (one MXFP4 block): K % 128 != 0
+    # runs on the register-staged kernels, whose last K stage is partly
+    # empty (zero codes with zero scales; the scale words of a row are then
+    # read byte by byte).  Every GEMM form, against the oracle.
+    M, N = 70, 130
+    x = synth.heavy_tailed_f32(260 + K, 261, (M, K))
+    w = synth.normal_f32(262 + K, (N, K), 0.02)
+    L = fp4q()
+    print(f"K = {K}", flush=True)
+    # NVFP4 prefill
+    ac, as_, at = _nv_gpu(dev_f32(x))
+    bc, bs, bt = _nv_gpu(dev_f32(w))
+    cx, sx, tx = ONV.quantize(x)
+    cw, sw, tw = ONV.quantize(w)
+    _check(host(L.gemm_w4a4(L.NVFP4, ac, as_, at, bc, bs, bt)), OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw),
+           f"nvfp4 {M}x{N}x{K}")
+    # MXFP4 prefill
+    mc, ms = L.quantize_mxfp4(dev_f32(x), None, True)
+    nc, ns = L.quantize_mxfp4(dev_f32(w), None, True)
+    rc, rs = OMX.quantize(OMX.hadamard32_scale(x))
+    qc, qs = OMX.quantize(OMX.hadamard32_scale(w))
+    _check(host(L.gemm_w4a4(L.MXFP4, mc, ms, None, nc, ns, None)), OG.w4a4_mxfp4(rc, rs, qc, qs),
+           f"mxfp4 {M}x{N}x{K}")
+    # W4A16
+    xb = synth.f32_to_bf16_bits(x)
+    _check(host(L.gemm_w4a16(dev_bf16(xb), bc, bs, bt)), OG.w4a16(xb, cw, sw, tw), f"w4a16 {M}x{N}x{K}")
+    # decode: row-streamed (M <= 4) and register-staged (M > 4) forms, fused
+    # and unfused, bit for bit with each other
+    for m in (1, 3, 8, 16):
+        yf, tf = L.linear_w4a4(dev_bf16(xb[:m]), bc, bs, bt)
+        a2, s2, t2 = L.quantize_nvfp4(dev_bf16(xb[:m]))
+        yu = L.gemm_w4a4(L.NVFP4, a2, s2, t2, bc, bs, bt)
+        assert_bytes_equal(host(yf).view(np.uint32), host(yu).view(np.uint32), f"fused vs unfused K={K} M={m}")
+        cxm, sxm, txm = ONV.quantize(OF.bf16_bits_to_f32(xb[:m]))
+        _check(host(yf), OG.w4a4_nvfp4(cxm, sxm, txm, cw, sw, tw), f"decode K={K} M={m}")
 
 
 def test_gemm_zero_and_one_hot():

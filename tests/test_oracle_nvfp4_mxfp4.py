@@ -224,6 +224,54 @@ def test_balance_scale_closed_form():
     assert np.allclose(t32.astype(np.float64) * u32, 1, rtol=2e-7)
 
 
+# Hand-worked values of the balance scale ("MACaQ", core method step (i):
+# t = sigma_W^0.75 / rms_x^0.25, range-clipped).  Each column below is built
+# so that sigma (population std over the weight rows) and rms are exact
+# powers of two, zero, or fixed values; the expected t is written out here,
+# not recomputed with the oracle's formula.
+def _balance_columns():
+    # W: 4 rows; X: 4 rows.  Column j: (W column, X column, expected t)
+    cols = [
+        ([16, -16, 16, -16], [16, 16, -16, 16], 4.0),            # 16^0.75 / 16^0.25 = 8 / 2
+        ([256, -256, 256, -256], [1, -1, 1, 1], 64.0),           # 256^0.75 / 1 = 2^6
+        ([1, -1, -1, 1], [256, 256, 256, -256], 0.25),           # 1 / 256^0.25 = 2^-2
+        ([5, 5, 5, 5], [1, 1, -1, 1], 2.0 ** -16),               # sigma = 0 -> 1e-12: t = 1e-9, clipped up
+        ([1024, -1024, 1024, -1024], [0, 0, 0, 0], 2.0 ** 16),   # rms = 0 -> 1e-12: t = 181019, clipped down
+        ([1, -1, 1, -1], [0, 0, 0, 0], 1000.0),                  # rms floor 1e-12 -> 1 / (1e-12)^0.25 = 1000
+        ([2, -2, 2, -2], [16, -16, 16, -16], 2.0 ** -0.25),      # 2^(0.75 - 1)
+        ([3, 3, -1, -1], [2, 2, 2, 2], 2.0 ** 0.5),             # sigma 2 (mean 1), rms 2: 2^(0.75 - 0.25)
+    ]
+    w = np.array([c[0] for c in cols], dtype=np.float64).T.copy()
+    x = np.array([c[1] for c in cols], dtype=np.float64).T.copy()
+    return w, x, np.array([c[2] for c in cols])
+
+
+def test_balance_scale_hand_worked_values():
+    w, x, want = _balance_columns()
+    t64, t32, u32 = balance.balance_scale(w, x)
+    exact = [0, 1, 2, 3, 4]                  # powers of two: no rounding anywhere
+    assert np.array_equal(t64[exact], want[exact])
+    assert np.array_equal(t32[exact], want[exact].astype(np.float32))
+    assert np.array_equal(u32[exact], (1.0 / want[exact]).astype(np.float32))
+    # the rest are one or two fp64 roundings away from the written-out value
+    assert np.allclose(t64, want, rtol=4e-16, atol=0)
+
+
+def test_balance_scale_orientation_and_population_std():
+    # alpha belongs to sigma_W: swapping the exponents would give
+    # 16^0.25 / 256^0.75 = 2^-4 for this column instead of 2^4
+    w = np.array([[16.0], [-16.0]])
+    x = np.array([[256.0], [256.0]])
+    t64, _, _ = balance.balance_scale(w, x)
+    assert t64[0] == 2.0 ** 3 / 2.0 ** 2
+    # population std (ddof = 0): +-2 over 4 rows is exactly 2 (the sample std
+    # would be 2 sqrt(4/3))
+    w = np.array([[2.0], [-2.0], [2.0], [-2.0]])
+    x = np.ones((4, 1))
+    t64, _, _ = balance.balance_scale(w, x)
+    assert t64[0] == 2.0 ** 0.75
+
+
 # ------------------------------------------------ NVFP4, 4/6 block scales ----
 # loopquant page, section 2.2 (the 4/6 block scaling keeps |x/s| <= 6 with
 # the block maximum mapped to 6 or to 4) and the section 2.5 listing
