@@ -74,6 +74,19 @@ int check_input(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, 
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Argument checks shared by both forms of the MACaQ refinement.
+int check_macaq(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lambda, int k_iters,
+                const uint8_t* codes, const uint8_t* scales) {
+  if (!w || !h || !codes || !scales) return fail(FP4Q_ERR_NULL_PTR, "w, h, codes and scales are required");
+  if (m < 1 || n < 32 || n % 32 || n > 16384 || ldw < n || ldw % 4)
+    return fail(FP4Q_ERR_BAD_SHAPE, "bad shape (m >= 1, n % 32 == 0, 32 <= n <= 16384, ldw >= n, ldw % 4 == 0)");
+  if (m > (int64_t(1) << 40) / ldw) return fail(FP4Q_ERR_BAD_SHAPE, "w too large");
+  if (!aligned16(w) || !aligned16(codes)) return fail(FP4Q_ERR_BAD_ALIGN, "w and codes must be 16-byte aligned");
+  if (!(lambda >= 0.0) || lambda > 1e300) return fail(FP4Q_ERR_BAD_ARG, "lambda must be finite and >= 0");
+  if (k_iters < 0 || k_iters > (1 << 20)) return fail(FP4Q_ERR_BAD_ARG, "k_iters must be in [0, 2^20]");
+  return FP4Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,21 +337,28 @@ int fp4q_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const d
                       int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, void* workspace,
                       int64_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
-  if (!w || !h || !codes || !scales || !workspace)
-    return fail(FP4Q_ERR_NULL_PTR, "w, h, codes, scales and workspace are required");
-  if (m < 1 || n < 32 || n % 32 || n > 16384 || ldw < n || ldw % 4)
-    return fail(FP4Q_ERR_BAD_SHAPE, "bad shape (m >= 1, n % 32 == 0, 32 <= n <= 16384, ldw >= n, ldw % 4 == 0)");
-  if (m > (int64_t(1) << 40) / ldw) return fail(FP4Q_ERR_BAD_SHAPE, "w too large");
-  if (!aligned16(w) || !aligned16(codes)) return fail(FP4Q_ERR_BAD_ALIGN, "w and codes must be 16-byte aligned");
+  if (!workspace) return fail(FP4Q_ERR_NULL_PTR, "workspace is required");
+  if (int st = check_macaq(w, m, n, ldw, h, lambda, k_iters, codes, scales)) return st;
   if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(FP4Q_ERR_BAD_ALIGN, "workspace must be 8-byte aligned");
-  if (!(lambda >= 0.0) || lambda > 1e300) return fail(FP4Q_ERR_BAD_ARG, "lambda must be finite and >= 0");
-  if (k_iters < 0 || k_iters > (1 << 20)) return fail(FP4Q_ERR_BAD_ARG, "k_iters must be in [0, 2^20]");
   if (workspace_bytes < fp4q_macaq_workspace_bytes(m, n))
     return fail(FP4Q_ERR_BAD_ARG, "workspace too small (%lld bytes needed)", (long long)fp4q_macaq_workspace_bytes(m, n));
   if (int st = check_device()) return st;
   return launch_status(fp4q::launch_macaq_refine(w, m, n, ldw, h, lambda, k_iters, codes, scales, flips,
                                                  static_cast<double*>(workspace), as_stream(stream)),
                        "macaq_refine");
+}
+
+int fp4q_macaq_refine_noalloc(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lambda,
+                              int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, void* stream) {
+  g_last_error[0] = 0;
+  if (int st = check_macaq(w, m, n, ldw, h, lambda, k_iters, codes, scales)) return st;
+  if (fp4q::macaq_scratch_rows(n) < 1)
+    return fail(FP4Q_ERR_BAD_ARG, "n = %lld: one row does not fit the %lld-byte static workspace", (long long)n,
+                (long long)(8 * fp4q::kMacaqScratchDoubles));
+  if (int st = check_device()) return st;
+  return launch_status(fp4q::launch_macaq_refine_static(w, m, n, ldw, h, lambda, k_iters, codes, scales, flips,
+                                                        as_stream(stream)),
+                       "macaq_refine_noalloc");
 }
 
 int fp4q_gemm_w4a4(int fmt, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,

@@ -45,6 +45,15 @@ hipError_t launch_hessian(const float* x, int64_t T, int64_t n, int64_t ldx, dou
 hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lam,
                                int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, double* ws,
                                hipStream_t s);
+// The same refinement with the workspace in a static per-device array of
+// kMacaqScratchDoubles float64 (16 MiB): the ridge once, then the rows in
+// passes of macaq_scratch_rows(n) rows.  Calls that overlap on one device
+// race on that array.
+constexpr int64_t kMacaqScratchDoubles = int64_t(1) << 21;
+int64_t macaq_scratch_rows(int64_t n);
+hipError_t launch_macaq_refine_static(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h,
+                                      double lam, int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips,
+                                      hipStream_t s);
 
 hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* y,

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "codec.h"
 #include "internal.h"
 
@@ -397,10 +399,14 @@ hipError_t launch_hessian(const float* x, int64_t T, int64_t n, int64_t ldx, dou
   return hipGetLastError();
 }
 
-hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lam,
-                               int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, double* ws,
-                               hipStream_t s) {
-  hipLaunchKernelGGL(k_ridge, dim3(1), dim3(kThreads), 0, s, h, n, lam, ws);
+namespace {
+
+// Screen, gradient and flips for rows [0, m) of w / codes / scales / flips
+// (already offset by the caller); ws holds the ridge delta and diag(H_f)
+// from k_ridge and room for an m x n gradient after them.  Rows are
+// independent, so any split of the rows gives the same bytes.
+void launch_rows(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, int k_iters,
+                 uint8_t* codes, uint8_t* scales, int32_t* flips, double* ws, hipStream_t s) {
   hipLaunchKernelGGL(k_screen, dim3(cdiv(m * (n / 32), kThreads)), dim3(kThreads), 0, s, w, m, n, ldw, ws,
                      codes, scales);
   double* g = ws + kWsHd + ((n + 31) / 32) * 32;
@@ -418,6 +424,62 @@ hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw
   else if (n <= 4096) flip(k_flip<256, 16>, 256);
   else if (n <= 8192) flip(k_flip<512, 16>, 512);
   else flip(k_flip<1024, 16>, 1024);                  // n <= 16384
+}
+
+// Workspace of the no-allocation form: one array per device, loaded with
+// the code object and held until the process ends.  Host code never names
+// it as an address (the host-side symbol is only a stand-in); it uses the
+// device address that hipGetSymbolAddress returns, taken once per device.
+static __device__ __align__(256) double scratch[kMacaqScratchDoubles];
+
+hipError_t scratch_address(double** out) {
+  static std::mutex mu;
+  static double* addr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<double*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lam,
+                               int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, double* ws,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_ridge, dim3(1), dim3(kThreads), 0, s, h, n, lam, ws);
+  launch_rows(w, m, n, ldw, h, k_iters, codes, scales, flips, ws, s);
+  return hipGetLastError();
+}
+
+int64_t macaq_scratch_rows(int64_t n) {
+  if (n < 1) return 0;
+  return (kMacaqScratchDoubles - kWsHd - ((n + 31) / 32) * 32) / n;
+}
+
+hipError_t launch_macaq_refine_static(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h,
+                                      double lam, int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips,
+                                      hipStream_t s) {
+  const int64_t rows = macaq_scratch_rows(n);
+  if (rows < 1) return hipErrorInvalidValue;
+  double* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_ridge, dim3(1), dim3(kThreads), 0, s, h, n, lam, ws);
+  for (int64_t r0 = 0; r0 < m; r0 += rows) {
+    const int64_t mc = m - r0 < rows ? m - r0 : rows;
+    launch_rows(w + r0 * ldw, mc, n, ldw, h, k_iters, codes + r0 * (n / 2), scales + r0 * (n / 32),
+                flips ? flips + r0 : nullptr, ws, s);
+  }
   return hipGetLastError();
 }
 

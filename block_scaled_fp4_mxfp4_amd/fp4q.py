@@ -63,6 +63,7 @@ _SIGS = {
     "fp4q_hessian_accumulate": ([_p, _l, _l, _l, _p, _p], _i),
     "fp4q_macaq_workspace_bytes": ([_l, _l], _l),
     "fp4q_macaq_refine": ([_p, _l, _l, _l, _p, ctypes.c_double, _i, _p, _p, _p, _p, _l, _p], _i),
+    "fp4q_macaq_refine_noalloc": ([_p, _l, _l, _l, _p, ctypes.c_double, _i, _p, _p, _p, _p], _i),
     "fp4q_gemm_w4a4": ([_i, _p, _p, _p, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_gemm_w4a16": ([_p, _l, _p, _p, _p, _l, _l, _l, _p, _l, _p], _i),
     "fp4q_gemm_w4a16_grouped": ([ctypes.POINTER(W4A16Problem), _i, _p], _i),
@@ -252,6 +253,31 @@ def macaq_refine(w: torch.Tensor, h: torch.Tensor, lam: float = 1.0, k_iters: in
     _check(lib.fp4q_macaq_refine(_ptr(w), m, n, w.stride(0), _ptr(h), float(lam), int(k_iters), _ptr(codes),
                                  _ptr(scales), _ptr(flips), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(w.device)), "macaq_refine")
+    return codes, scales, flips
+
+
+def macaq_refine_noalloc(w: torch.Tensor, h: torch.Tensor, lam: float = 1.0, k_iters: int = 128,
+                         out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """macaq_refine with the library's static per-device workspace: no
+    device allocation when the outputs (codes, scales, flips) are passed in
+    `out`.  Calls that overlap on one device race on that workspace."""
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be fp32 [m, n] with unit column stride")
+    if h.dtype != torch.float64 or not h.is_contiguous():
+        raise ValueError("h must be contiguous float64 [n, n]")
+    m, n = w.shape
+    if out is None:
+        out = (torch.empty((m, n // 2), dtype=torch.uint8, device=w.device),
+               torch.empty((m, n // 32), dtype=torch.uint8, device=w.device),
+               torch.empty(m, dtype=torch.int32, device=w.device))
+    codes, scales, flips = out
+    if (codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or flips.dtype != torch.int32
+            or not (codes.is_contiguous() and scales.is_contiguous() and flips.is_contiguous())
+            or codes.shape != (m, n // 2) or scales.shape != (m, n // 32) or flips.shape != (m,)):
+        raise ValueError("out must be contiguous (uint8 [m, n/2], uint8 [m, n/32], int32 [m])")
+    _check(lib.fp4q_macaq_refine_noalloc(_ptr(w), m, n, w.stride(0), _ptr(h), float(lam), int(k_iters),
+                                         _ptr(codes), _ptr(scales), _ptr(flips), _stream(w.device)),
+           "macaq_refine_noalloc")
     return codes, scales, flips
 
 

@@ -348,6 +348,24 @@ int fp4q_macaq_refine(const float* w, int64_t m, int64_t n, int64_t ldw, const d
                       int64_t workspace_bytes, void* stream);
 
 /*
+ * fp4q_macaq_refine for callers that cannot allocate device memory (code
+ * under stream capture, serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, and the same output bytes.
+ * The workspace is a static array of 16 MiB per device, loaded with the
+ * library's code object and held until the process ends; this call makes
+ * no allocation.  Rows pass through it in chunks of
+ * (2^21 - 32 - n) / n rows (510 at n = 4096, 126 at n = 16384), each chunk
+ * on the same four kernels, so every m is accepted; n above 16384 (as for
+ * fp4q_macaq_refine) is rejected with FP4Q_ERR_BAD_SHAPE.
+ * Nothing in the array needs to start at zero: each call writes what it
+ * reads.  Every call on one device shares that device's array and leaves
+ * its contents behind: calls that overlap on one device (two streams, two
+ * threads) race and give undefined results; serialise them.
+ */
+int fp4q_macaq_refine_noalloc(const float* w, int64_t m, int64_t n, int64_t ldw, const double* h, double lambda,
+                              int k_iters, uint8_t* codes, uint8_t* scales, int32_t* flips, void* stream);
+
+/*
  * W4A4 GEMM over quantized operands: Y = dequant(A) * dequant(B)^T, fp32
  * accumulate, fp32 out.  [MQ] "Core method" (y = [(x*t)B]_MXFP4 W'^T_MXFP4)
  * and [GDN] "NVFP4 and W4A4" (both operands NVFP4, GEMM on the 4-bit data).

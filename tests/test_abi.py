@@ -179,6 +179,24 @@ def test_macaq_validation(fp4q):
     assert b"workspace" in L.fp4q_last_error()
 
 
+def test_macaq_noalloc_validation(fp4q):
+    L = fp4q.lib
+    P = ctypes.c_void_p
+    f16, f8 = P(0x10000), P(0x10008)
+    ok = dict(w=f16, m=10, n=64, ldw=64, h=f16, lam=1.0, k=128, codes=f16, scales=f16, flips=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.fp4q_macaq_refine_noalloc(a["w"], a["m"], a["n"], a["ldw"], a["h"], a["lam"], a["k"],
+                                           a["codes"], a["scales"], a["flips"], None)
+
+    assert call(w=None) == 1 and call(scales=None) == 1
+    assert call(n=48) == 2 and call(n=16416, ldw=16416) == 2 and call(m=0) == 2
+    assert b"16384" in L.fp4q_last_error()
+    assert call(w=P(0x10004)) == 3 and call(codes=f8) == 3
+    assert call(lam=-1.0) == 5 and call(k=(1 << 20) + 1) == 5
+
+
 def test_w4a16_grouped_validation(fp4q):
     L, P = fp4q.lib, fp4q.W4A16Problem
     f16 = 0x10000
