@@ -23,9 +23,10 @@
 //    never stored), so every lane issues the same number of loads and the
 //    wait counts are compile-time constants;
 //  * the fp32 output leaves through LDS: each wavefront re-stages 16-row
-//    strips of its accumulators and writes whole rows with 16-byte
-//    non-temporal stores (scattered 4-byte lane stores ran at ~2.3 TB/s and
-//    cost as much time as the whole K loop).
+//    strips of its accumulators and writes whole rows with 16-byte stores
+//    (scattered 4-byte lane stores ran at ~2.3 TB/s and cost as much time
+//    as the whole K loop); the NVFP4 and W4A16 forms make those stores
+//    non-temporal, the MXFP4 form ordinary (FP4Q_EPI_NT, FP4Q_EPI_NT_MX).
 
 #include <hip/hip_runtime.h>
 
