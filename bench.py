@@ -17,6 +17,7 @@ Sigma-Delta + W4A16, the tiny NVFP4 case) with their own rooflines.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
                        [--no-cpu-baseline] [--only-step]
        python bench.py --extras mxfp4,decode,... [--quick]    (one row alone, for profiling)
+       python bench.py --hbm-ceiling | --calibrate-copy        (reference streams)
 """
 from __future__ import annotations
 
@@ -119,6 +120,8 @@ def parse():
                         "mxfp4, macaq, nvfp4_46, harmonize, decode, sigma_delta, tiny")
     p.add_argument("--quick", action="store_true",
                    help="extras: 1 warm-up and at most 3 timed calls per operation (for profiling)")
+    p.add_argument("--hbm-ceiling", action="store_true",
+                   help="run only torch's copy, fill and sum on rotated buffers (practical HBM rates of this box)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (HBM byte-counter calibration)")
     return p.parse_args()
@@ -149,6 +152,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                           "launches": 3}), flush=True)
+        return
+
+    if args.hbm_ceiling:
+        print(json.dumps(hbm_ceiling(torch, stream)), flush=True)
         return
 
     from block_scaled_fp4_mxfp4_amd import fp4q as L, synth
@@ -326,12 +333,39 @@ def _kernel_hash():
     return h.hexdigest()
 
 
+def hbm_ceiling(torch, stream):
+    """Streaming rates of the platform's own copy, fill and sum kernels on
+    buffers rotated past the 256 MB last-level cache: what a plain
+    memory-bound kernel reaches on this machine, beside the 8 TB/s spec."""
+    out = {}
+    for mb in (42, 105, 256):
+        n = mb * (1 << 20) // 4
+        c = max(3, -(-1100 // mb))
+        src = [torch.ones(n, device="cuda:0") for _ in range(c)]
+        dst = [torch.empty(n, device="cuda:0") for _ in range(c)]
+        nbytes = n * 4
+        tc = _time_op(torch, stream, lambda i: dst[i % c].copy_(src[i % c]), 30)
+        tf = _time_op(torch, stream, lambda i: dst[i % c].fill_(2.0), 30)
+        ts = _time_op(torch, stream, lambda i: src[i % c].sum(), 30)
+        out[f"{mb}MB_x{c}"] = {"copy_GBps": round(2 * nbytes / (tc["median_ms"] * 1e-3) / 1e9, 1),
+                               "fill_GBps": round(nbytes / (tf["median_ms"] * 1e-3) / 1e9, 1),
+                               "sum_read_GBps": round(nbytes / (ts["median_ms"] * 1e-3) / 1e9, 1)}
+        del src, dst
+        torch.cuda.empty_cache()
+    return {"hbm_ceiling": out, "spec_GBps": PEAK["hbm_GBps"]}
+
+
 # ---------------------------------------------------------------- extras ----
 
 QUICK = False
 
 
 def _time_op(torch, stream, fn, iters, warm=3):
+    """GPU time per call, back to back: the calls run in batches between
+    two events (no event between calls of a batch), behind a short device
+    sleep that lets the host queue every call first, so host-side launch
+    cost does not show as device time.  Returns the median, p10 and p90 of
+    the per-call time over the batches."""
     if QUICK:
         iters, warm = min(iters, 3), 1
     t0 = time.perf_counter()
@@ -342,14 +376,21 @@ def _time_op(torch, stream, fn, iters, warm=3):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        fn(i)
-        b.record(stream)
+    nb = min(iters, 7)
+    per = max(1, iters // nb)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    torch.cuda._sleep(10_000_000)                          # ~5 ms: the host queues the batches meanwhile
+    evs[0].record(stream)
+    k = 0
+    for j in range(nb):
+        for _ in range(per):
+            fn(k)
+            k += 1
+        evs[j + 1].record(stream)
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
-    return {"median_ms": ts[len(ts) // 2], "p10_ms": ts[len(ts) // 10], "p90_ms": ts[(9 * len(ts)) // 10]}
+    ts = sorted(evs[j].elapsed_time(evs[j + 1]) / per for j in range(nb))
+    return {"median_ms": ts[len(ts) // 2], "p10_ms": ts[len(ts) // 10], "p90_ms": ts[(9 * len(ts)) // 10],
+            "calls": nb * per}
 
 
 def _bw(t, nbytes):
