@@ -270,11 +270,12 @@ def main():
         if t.get("kernel_source_sha256") == _kernel_hash():
             traffic = t.get("bytes_per_launch")
 
-    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK["fp16_TFLOPs"],
-                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK["fp16_TFLOPs"], 4), "traffic": traffic,
+    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK["fp4_TFLOPs"],
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK["fp4_TFLOPs"], 4), "traffic": traffic,
                 "kernel": "k_gemm_mx3<FMT_NV, 256, 320, 64, 1, 8, 2, M32 = 1> (8 wavefronts, 256x320 tiles, LDS-DMA tiles, exact NVFP4 dequant, 32x32x16 fp16 MFMA)",
                 "algorithmic": "2*M*N*K flop per launch (M=4096, N=10240, K=5120)",
-                "frac_of_fp4_peak": round(gemm_tflops / PEAK["fp4_TFLOPs"], 4)}
+                "instruction_peak": {"dtype": "fp16 MFMA (exact NVFP4 products need 6 significant bits)",
+                                     "peak": PEAK["fp16_TFLOPs"], "frac": round(gemm_tflops / PEAK["fp16_TFLOPs"], 4)}}
 
     out = {
         "metric": "W4A4 FP4 GEMM TFLOP/s + quantizer GB/s, fraction of MI355X roofline",
@@ -315,6 +316,12 @@ def main():
         del xs, ws_, xqs, wqs, y, x0, w0
         torch.cuda.empty_cache()
         out["extras"] = run_extras(L, synth, np, torch, dev, stream, log)
+        g = out["extras"].get("mxfp4_transform_2048x14336x4096", {}).get("gemm_mxfp4")
+        if g:
+            out["roofline_mxfp4_gemm"] = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": PEAK["fp4_TFLOPs"],
+                                          "unit": "TFLOP/s", "frac": g["frac"],
+                                          "kernel": "k_gemm_mx3<FMT_MX, 256, 224, 128> (scaled FP4 MFMA 16x16x128)",
+                                          "workload": "MXFP4 GEMM 2048x14336x4096, operands rotated"}
 
     if not args.only_step and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, M, N, K, log)
@@ -499,6 +506,11 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
         for r, key in (("6", "max_to_6"), ("4/6", "four_six")):
             fs[key] = _bw(_time_op(torch, stream, lambda i: L.quantize_nvfp4(ws[i % reps], rule=r, out=outs[r][i % reps]), 30),
                           nbytes)
+        # a static tensor scale (given by the caller): one pass, no amax
+        fs["max_to_6_static_scale"] = _bw(_time_op(torch, stream, lambda i: L.quantize_nvfp4(
+            ws[i % reps], tensor_scale=outs["6"][i % reps][2], out=outs["6"][i % reps]), 30), nbytes)
+        fs["note"] = ("dynamic: amax pass (reads the tensor) + finalize + quantize pass (reads it again); "
+                      "GBps counts the tensor read once")
         ex["nvfp4_46_quantize_w_10240x5120"] = fs
         del ws, outs, wb
         torch.cuda.empty_cache()
