@@ -79,7 +79,7 @@ int check_macaq(const float* w, int64_t m, int64_t n, int64_t ldw, const double*
                 const uint8_t* codes, const uint8_t* scales) {
   if (!w || !h || !codes || !scales) return fail(FP4Q_ERR_NULL_PTR, "w, h, codes and scales are required");
   if (m < 1 || n < 32 || n % 32 || n > 16384 || ldw < n || ldw % 4)
-    return fail(FP4Q_ERR_BAD_SHAPE, "bad shape (m >= 1, n % 32 == 0, 32 <= n <= 16384, ldw >= n, ldw % 4 == 0)");
+    return fail(FP4Q_ERR_BAD_SHAPE, "bad shape (m >= 1, n %% 32 == 0, 32 <= n <= 16384, ldw >= n, ldw %% 4 == 0)");
   if (m > (int64_t(1) << 40) / ldw) return fail(FP4Q_ERR_BAD_SHAPE, "w too large");
   if (!aligned16(w) || !aligned16(codes)) return fail(FP4Q_ERR_BAD_ALIGN, "w and codes must be 16-byte aligned");
   if (!(lambda >= 0.0) || lambda > 1e300) return fail(FP4Q_ERR_BAD_ARG, "lambda must be finite and >= 0");
