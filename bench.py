@@ -118,6 +118,8 @@ def parse():
     p.add_argument("--extras", default=None,
                    help="comma list of extras to run alone, without the headline step (for profiling): "
                         "mxfp4, macaq, nvfp4_46, harmonize, decode, sigma_delta, tiny")
+    p.add_argument("--seed", type=int, default=0,
+                   help="input set: 0 is the default synthetic data; s > 0 offsets every generator seed")
     p.add_argument("--quick", action="store_true",
                    help="extras: 1 warm-up and at most 3 timed calls per operation (for profiling)")
     p.add_argument("--hbm-ceiling", action="store_true",
@@ -159,6 +161,8 @@ def main():
         return
 
     from block_scaled_fp4_mxfp4_amd import fp4q as L, synth
+    global SEED
+    SEED = args.seed
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -176,7 +180,7 @@ def main():
 
     # ------------------------------------------------------------ headline
     log("generating the prefill workload (X 4096x5120, W 10240x5120 bf16)")
-    wl = synth.nvfp4_prefill()
+    wl = synth.nvfp4_prefill(seed=SEED)
     M, N, K = wl.meta["M"], wl.meta["N"], wl.meta["K"]
     x0 = bf16(wl.arrays["x_bf16"])
     w0 = bf16(wl.arrays["w_bf16"])
@@ -282,7 +286,7 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "warmup_steps_run": n_warm, "dtype": "nvfp4 (e2m1+e4m3, fp16 mfma, fp32 acc)",
-        "data": "synthetic (seeded heavy-tailed activations, N(0,0.02^2) weights)",
+        "data": f"synthetic (seeded heavy-tailed activations, N(0,0.02^2) weights; input set {SEED})",
         "config": {"workload": "nvfp4_prefill X[4096x5120] W[10240x5120] bf16 -> quantize both -> GEMM",
                    "M": M, "N": N, "K": K, "parallelism": "single GPU"},
         "roofline": roofline,
@@ -365,6 +369,7 @@ def hbm_ceiling(torch, stream):
 # ---------------------------------------------------------------- extras ----
 
 QUICK = False
+SEED = 0
 
 
 def _time_op(torch, stream, fn, iters, warm=3):
@@ -424,7 +429,7 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
     # ---------------- MXFP4 with the online transform (2048 x 14336 x 4096)
     if want("mxfp4"):
         log("extras: MXFP4 + transform")
-        wl = synth.mxfp4_transform()
+        wl = synth.mxfp4_transform(seed=SEED)
         M, N, K = wl.meta["M"], wl.meta["N"], wl.meta["K"]
         x, w = bf16(wl.arrays["x_bf16"]), bf16(wl.arrays["w_bf16"])
         del wl
@@ -463,7 +468,7 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
     if want("macaq"):
         # (14336 x 4096) on its 2048 calibration rows, both transformed
         log("extras: MACaQ Hessian + exponent screen + Flip-Refinement")
-        wl = synth.mxfp4_transform()
+        wl = synth.mxfp4_transform(seed=SEED)
         M, N, K = wl.meta["M"], wl.meta["N"], wl.meta["K"]
         x, w = bf16(wl.arrays["x_bf16"]), bf16(wl.arrays["w_bf16"])
         del wl
@@ -495,7 +500,7 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
     # ---------------- NVFP4 4/6 block scales on the prefill weight (10240 x 5120)
     if want("nvfp4_46"):
         log("extras: NVFP4 4/6 block scales")
-        wl = synth.nvfp4_prefill()
+        wl = synth.nvfp4_prefill(seed=SEED)
         wb = bf16(wl.arrays["w_bf16"])
         del wl
         reps = 5                                       # 5 x 105 MB in rotation, past 512 MB
@@ -547,7 +552,7 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
     # ---------------- NVFP4 decode (N 17408, K 5120, M in 1, 4, 16)
     if want("decode"):
         log("extras: NVFP4 decode")
-        wl = synth.nvfp4_decode()
+        wl = synth.nvfp4_decode(seed=SEED)
         N, K = wl.meta["N"], wl.meta["K"]
         wd = torch.from_numpy(wl.arrays["w"]).to(dev)
         copies = 11                                    # 11 x 50 MB > 512 MB: defeats the 256 MB cache
@@ -578,7 +583,7 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
     # ---------------- looped core: Sigma-Delta requant + W4A16 GEMMs, R = 32
     if want("sigma_delta"):
         log("extras: looped Sigma-Delta")
-        wl = synth.looped_sigma_delta()
+        wl = synth.looped_sigma_delta(seed=SEED)
         shapes = wl.meta["shapes"]
         segs, gem = [], []
         h = bf16(wl.arrays["h_bf16"])
@@ -660,7 +665,7 @@ def run_extras(L, synth, np, torch, dev, stream, log, only=None):
 
     # ---------------- tiny NVFP4 (latency only)
     if want("tiny"):
-        wl = synth.nvfp4_tiny()
+        wl = synth.nvfp4_tiny(seed=SEED)
         xt = torch.from_numpy(wl.arrays["x"]).to(dev)
         wt = torch.from_numpy(wl.arrays["w"]).to(dev)
         bq = L.quantize_nvfp4(wt)
@@ -760,7 +765,7 @@ def cpu_baseline_configs(log):
     # MXFP4 with the online transform: balance statistic on the full tensors,
     # transform + quantize on 512 rows of X and 1536 rows of W, GEMM 512 x 1536
     log("cpu baseline: MXFP4 + transform stages")
-    wl = synth.mxfp4_transform()
+    wl = synth.mxfp4_transform(seed=SEED)
     M, N, K = wl.meta["M"], wl.meta["N"], wl.meta["K"]
     xf = OF.bf16_bits_to_f32(wl.arrays["x_bf16"])
     wf = OF.bf16_bits_to_f32(wl.arrays["w_bf16"])
@@ -786,7 +791,7 @@ def cpu_baseline_configs(log):
     # NVFP4 decode: activation quantize of M rows, GEMM against 1024
     # quantized rows of W (W is quantized once, outside the step)
     log("cpu baseline: NVFP4 decode stages")
-    wl = synth.nvfp4_decode()
+    wl = synth.nvfp4_decode(seed=SEED)
     N, K = wl.meta["N"], wl.meta["K"]
     wrows = 1024
     cw, sw, tw = ONV.quantize(wl.arrays["w"][:wrows])
@@ -809,7 +814,7 @@ def cpu_baseline_configs(log):
     # the first linear, and the W4A16 GEMM of one full 768 x 768 linear on
     # the [4096 x 768] hidden state
     log("cpu baseline: looped Sigma-Delta stages")
-    wl = synth.looped_sigma_delta()
+    wl = synth.looped_sigma_delta(seed=SEED)
     shapes = wl.meta["shapes"]
     nw = sum(n * k for n, k in shapes)
     w0 = wl.arrays["w0"]

@@ -78,6 +78,11 @@ LOOPED_SHAPES: List[Tuple[int, int]] = [
 ]
 
 
+# Workload seeds: seed 0 is the default input set; seed s adds
+# SEED_STRIDE * s to every generator seed of the workload.
+SEED_STRIDE = 100_000
+
+
 @dataclass
 class Workload:
     name: str
@@ -85,53 +90,58 @@ class Workload:
     meta: Dict[str, object] = field(default_factory=dict)
 
 
-def nvfp4_tiny() -> Workload:
+def nvfp4_tiny(seed: int = 0) -> Workload:
     """NVFP4 W4A4 linear, tiny: X fp32 [64x256] N(0,1) with 2 outlier
     channels x50; W fp32 [256x256] N(0, 0.02**2)."""
-    x = heavy_tailed_f32(1001, 1003, (64, 256), count=2, factor=50.0)
-    w = normal_f32(1002, (256, 256), 0.02)
+    o = SEED_STRIDE * seed
+    x = heavy_tailed_f32(1001 + o, 1003 + o, (64, 256), count=2, factor=50.0)
+    w = normal_f32(1002 + o, (256, 256), 0.02)
     return Workload("nvfp4_tiny_64x256x256", {"x": x, "w": w},
                     {"M": 64, "N": 256, "K": 256})
 
 
-def nvfp4_prefill(m: int = 4096, n: int = 10240, k: int = 5120) -> Workload:
+def nvfp4_prefill(m: int = 4096, n: int = 10240, k: int = 5120, seed: int = 0) -> Workload:
     """NVFP4 prefill linear: X bf16 [4096x5120] heavy-tailed; W bf16
     generated as [K x N] = [5120x10240] N(0, 0.02**2) and stored [N x K]."""
-    x = f32_to_bf16_bits(heavy_tailed_f32(2001, 2003, (m, k)))
-    w_kn = normal_f32(2002, (k, n), 0.02)
+    o = SEED_STRIDE * seed
+    x = f32_to_bf16_bits(heavy_tailed_f32(2001 + o, 2003 + o, (m, k)))
+    w_kn = normal_f32(2002 + o, (k, n), 0.02)
     w = f32_to_bf16_bits(np.ascontiguousarray(w_kn.T))
     return Workload(f"nvfp4_prefill_{m}x{n}x{k}", {"x_bf16": x, "w_bf16": w},
                     {"M": m, "N": n, "K": k})
 
 
-def mxfp4_transform(m: int = 2048, n: int = 14336, k: int = 4096) -> Workload:
+def mxfp4_transform(m: int = 2048, n: int = 14336, k: int = 4096, seed: int = 0) -> Workload:
     """MXFP4 linear with online transform: X bf16 [2048x4096] heavy-tailed,
     W bf16 [14336x4096] N(0, 0.02**2)."""
-    x = f32_to_bf16_bits(heavy_tailed_f32(3001, 3003, (m, k)))
-    w = f32_to_bf16_bits(normal_f32(3002, (n, k), 0.02))
+    o = SEED_STRIDE * seed
+    x = f32_to_bf16_bits(heavy_tailed_f32(3001 + o, 3003 + o, (m, k)))
+    w = f32_to_bf16_bits(normal_f32(3002 + o, (n, k), 0.02))
     return Workload(f"mxfp4_transform_{m}x{n}x{k}", {"x_bf16": x, "w_bf16": w},
                     {"M": m, "N": n, "K": k})
 
 
-def nvfp4_decode(n: int = 17408, k: int = 5120, m_max: int = 16) -> Workload:
+def nvfp4_decode(n: int = 17408, k: int = 5120, m_max: int = 16, seed: int = 0) -> Workload:
     """NVFP4 decode: X bf16 [16x5120] heavy-tailed (the first M rows are
     used, M in {1, 4, 16}); W fp32 [17408x5120] N(0, 0.02**2), quantized
     once outside the timed region."""
-    x = f32_to_bf16_bits(heavy_tailed_f32(4001, 4003, (m_max, k)))
-    w = normal_f32(4002, (n, k), 0.02)
+    o = SEED_STRIDE * seed
+    x = f32_to_bf16_bits(heavy_tailed_f32(4001 + o, 4003 + o, (m_max, k)))
+    w = normal_f32(4002 + o, (n, k), 0.02)
     return Workload(f"nvfp4_decode_{n}x{k}", {"x_bf16": x, "w": w},
                     {"N": n, "K": k, "M_list": [1, 4, 16]})
 
 
-def looped_sigma_delta(tokens: int = 4096) -> Workload:
+def looped_sigma_delta(tokens: int = 4096, seed: int = 0) -> Workload:
     """Looped core: 13 fp32 masters N(0, 0.02**2) (seed 5002 + 10 i), hidden
     state bf16 [8x512x768] = [4096x768] heavy-tailed, and a [4096x3072]
     heavy-tailed bf16 input for the down projection; R = 32 steps."""
+    o = SEED_STRIDE * seed
     arrays = {}
     for i, (n, k) in enumerate(LOOPED_SHAPES):
-        arrays[f"w{i}"] = normal_f32(5002 + 10 * i, (n, k), 0.02)
-    arrays["h_bf16"] = f32_to_bf16_bits(heavy_tailed_f32(5001, 5003, (tokens, 768)))
-    arrays["hd_bf16"] = f32_to_bf16_bits(heavy_tailed_f32(5011, 5013, (tokens, 3072)))
+        arrays[f"w{i}"] = normal_f32(5002 + 10 * i + o, (n, k), 0.02)
+    arrays["h_bf16"] = f32_to_bf16_bits(heavy_tailed_f32(5001 + o, 5003 + o, (tokens, 768)))
+    arrays["hd_bf16"] = f32_to_bf16_bits(heavy_tailed_f32(5011 + o, 5013 + o, (tokens, 3072)))
     return Workload("looped_sigma_delta_13x_R32", arrays,
                     {"R": 32, "tokens": tokens, "shapes": LOOPED_SHAPES})
 

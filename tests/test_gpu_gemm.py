@@ -41,8 +41,9 @@ def test_nvfp4_gemm_small_ragged(M, N, K):
     _check(y, OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), f"nvfp4 {M}x{N}x{K}")
 
 
-def test_nvfp4_tiny_config():
-    wl = synth.nvfp4_tiny()
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nvfp4_tiny_config(seed):
+    wl = synth.nvfp4_tiny(seed=seed)
     x, w = wl.arrays["x"], wl.arrays["w"]
     L = fp4q()
     ac, as_, at = _nv_gpu(dev_f32(x))
@@ -50,7 +51,7 @@ def test_nvfp4_tiny_config():
     y = host(L.gemm_w4a4(L.NVFP4, ac, as_, at, bc, bs, bt))
     cx, sx, tx = ONV.quantize(x)
     cw, sw, tw = ONV.quantize(w)
-    _check(y, OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), "nvfp4 tiny config")
+    _check(y, OG.w4a4_nvfp4(cx, sx, tx, cw, sw, tw), f"nvfp4 tiny config, input set {seed}")
 
 
 def test_nvfp4_gemm_wide_tiles_ragged():

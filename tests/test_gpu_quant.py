@@ -32,8 +32,9 @@ def test_abi_version_and_device():
     assert fp4q().abi_version() == 1
 
 
-def test_nvfp4_tiny_config_bit_exact():
-    wl = synth.nvfp4_tiny()
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nvfp4_tiny_config_bit_exact(seed):
+    wl = synth.nvfp4_tiny(seed=seed)
     for name in ("x", "w"):
         a = wl.arrays[name]
         _nv_check(a, dev_f32(a))
