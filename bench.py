@@ -110,8 +110,8 @@ class ClockSampler:
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
@@ -380,6 +380,8 @@ def _time_op(torch, stream, fn, iters, warm=3):
     the per-call time over the batches."""
     if QUICK:
         iters, warm = min(iters, 3), 1
+    else:
+        iters, warm = max(iters, 100), max(warm, 10)   # at least 10 warm-up and 100 timed calls
     t0 = time.perf_counter()
     n = 0
     while n < warm or (not QUICK and time.perf_counter() - t0 < 0.05):   # >= 50 ms of warm-up per operation
@@ -388,7 +390,7 @@ def _time_op(torch, stream, fn, iters, warm=3):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    nb = min(iters, 7)
+    nb = min(iters, 10)
     per = max(1, iters // nb)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda._sleep(10_000_000)                          # ~5 ms: the host queues the batches meanwhile
@@ -712,7 +714,18 @@ def _cores():
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = affinity
-    return min(blas_threads, affinity), affinity
+    return min(blas_threads, affinity), affinity, blas_threads
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(wl, M, N, K, log):
@@ -721,7 +734,7 @@ def cpu_baseline(wl, M, N, K, log):
     import numpy as np
     from oracle import formats as OF, nvfp4 as ONV, gemm as OG
 
-    cores, affinity = _cores()
+    cores, affinity, blas_threads = _cores()
     xs_rows, ws_rows, gn = 1024, 3072, 1024
     log(f"cpu baseline: oracle on {xs_rows} rows of X, {ws_rows} rows of W, GEMM {xs_rows}x{gn}x{K}")
     xf = OF.bf16_bits_to_f32(wl.arrays["x_bf16"][:xs_rows])
@@ -743,7 +756,7 @@ def cpu_baseline(wl, M, N, K, log):
                        f"{t1 - t0:.1f} s) and its float64 GEMM {xs_rows}x{gn}x{K} (BLAS, {t2 - t1:.2f} s); "
                        f"full-step time extrapolated per stage: {full_s:.1f} s"),
             "full_step_s_est": round(full_s, 2),
-            "host_cpu": platform.processor() or platform.machine(), "affinity_cores": affinity,
+            "host_cpu": _cpu_model(), "affinity_cores": affinity, "blas_threads": blas_threads,
             "threads_note": "quantization stages use 1 thread; the GEMM stage uses `cores` BLAS threads"}
 
 
