@@ -604,7 +604,8 @@ __device__ __forceinline__ void split_unit(float y, uint32_t& m, uint32_t& sh) {
 }
 
 // Access k >= 1 of the stateless two-point chain (F4b; two_point_prepare
-// once per element, two_point_pick once per access): lo, hi the E2M1
+// and two_point_start once per element, two_point_next once per access):
+// lo, hi the E2M1
 // neighbours of x, p = (x - lo) / (hi - lo); hi exactly when
 // floor(k p) - floor((k - 1) p) = 1.  Exact in integers for k < 2^24: x - lo
 // is exact in binary32 (lo = 0, or Sterbenz: lo <= x <= 2 lo in magnitude)
@@ -629,13 +630,26 @@ __device__ __forceinline__ void two_point_prepare(float x, uint32_t& w0, uint32_
   w0 = m | (lo_c << 24) | (neg0 ? 1u << 28 : 0u);
   w1 = sh;
 }
-__device__ __forceinline__ uint32_t two_point_pick(uint32_t w0, uint32_t w1, uint32_t k) {
+// The accesses run in order, so the difference of floors is a carry: with
+// T = 2^sh, bias = T - 1 on [-0.5, 0) (ceiling) else 0, and
+// r = ((k - 1) m + bias) mod T, floor((k m + bias) / T) -
+// floor(((k - 1) m + bias) / T) = [r + m >= T] (r < T and m <= T).
+// two_point_start gives r before access k0 + 1; two_point_next takes one
+// access: it adds m, reduces by the carry and picks the code.
+__device__ __forceinline__ uint64_t two_point_start(uint32_t w0, uint32_t w1, uint32_t k0) {
+  const uint32_t m = w0 & 0xFFFFFFu;
+  const bool neg0 = (w0 >> 28) & 1u;
+  const uint64_t t = uint64_t(1) << w1;
+  return ((uint64_t)k0 * m + (neg0 ? t - 1u : 0u)) & (t - 1u);
+}
+__device__ __forceinline__ uint32_t two_point_next(uint32_t w0, uint32_t w1, uint64_t& r) {
   const uint32_t m = w0 & 0xFFFFFFu, lo_c = (w0 >> 24) & 15u;
   const bool neg0 = (w0 >> 28) & 1u;
-  const uint64_t prod = (uint64_t)k * m, prev = prod - m;          // k m and (k - 1) m
-  const uint64_t bias = neg0 ? (uint64_t(1) << w1) - 1u : 0u;      // ceiling instead of floor
-  const uint64_t d = ((prod + bias) >> w1) - ((prev + bias) >> w1);
-  return (neg0 ? d == 0u : d == 1u) ? bracket_hi(lo_c) : lo_c;
+  const uint64_t t = uint64_t(1) << w1;
+  r += m;
+  const bool carry = r >= t;
+  r = carry ? r - t : r;
+  return carry != neg0 ? bracket_hi(lo_c) : lo_c;
 }
 
 // `steps` accesses of stochastic rounding at the fixed NVFP4 scale of each
@@ -687,15 +701,21 @@ __global__ __launch_bounds__(kThreads) void k_stochastic_round(const SdArgs args
       if (TWO_POINT) two_point_prepare(x[u][i], w0[u][i], w1[u][i]);
       else w0[u][i] = sr_prepare(x[u][i]);
     }
+  uint64_t tp_r[TWO_POINT ? kSdUnroll : 1][8];
+  if constexpr (TWO_POINT) {
+#pragma unroll
+    for (int u = 0; u < kSdUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tp_r[u][i] = two_point_start(w0[u][i], w1[u][i], step0);
+  }
   for (int k = 0; k < steps; ++k) {
 #pragma unroll
     for (int u = 0; u < kSdUnroll; ++u) {
       if (cidx[u] >= n) continue;
       uint32_t pk = 0;
-      if (TWO_POINT) {
-        const uint32_t acc = step0 + (uint32_t)k + 1u;
+      if constexpr (TWO_POINT) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pk |= two_point_pick(w0[u][i], w1[u][i], acc) << (4 * i);
+        for (int i = 0; i < 8; ++i) pk |= two_point_next(w0[u][i], w1[u][i], tp_r[u][i]) << (4 * i);
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {                    // two Philox groups of four elements
