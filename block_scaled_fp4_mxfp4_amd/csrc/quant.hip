@@ -541,8 +541,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;   // one 32x32->64 each
-    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input exclusive or in one instruction (truth table 0x96)
+    c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
