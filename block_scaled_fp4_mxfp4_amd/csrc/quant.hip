@@ -226,27 +226,63 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     cidx[u] = ((int64_t)blockIdx.x * kNvUnroll + u) * kThreads + threadIdx.x;
     load8<BF16>(x, chunk_offset<CONTIG>(clamp_chunk(cidx[u], nchunks), cpr, ld), v[u]);
   }
+  // Block maxima of every chunk (over the lane pair), then the block
+  // scales: both lanes of a pair need the scales of both of their blocks,
+  // so the even lane computes those of chunk u and the odd lane those of
+  // chunk u + 1, and each passes its results to the other (the same
+  // operations on the same operands, computed once per pair).
+  static_assert(kNvUnroll % 2 == 0, "chunks are paired");
+  const bool odd = threadIdx.x & 1;
+  float a[kNvUnroll];
 #pragma unroll
   for (int u = 0; u < kNvUnroll; ++u) {
-    float a = 0.0f;
+    a[u] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[u][i]));
-    a = fmaxf(a, dpp_xor1(a));                       // block max over the lane pair
-    uint32_t sb = 0;
-    if (a > 0.0f && st > 0.0f) sb = e4m3_ceil(a / six_st);
-    const float s = st * e4m3_decode(sb);
-    const float rho = 1.0f / s;
-    uint32_t p = (s == 0.0f) ? 0u : encode8_scaled(v[u], rho);
+    for (int i = 0; i < 8; ++i) a[u] = fmaxf(a[u], __builtin_fabsf(v[u][i]));
+    a[u] = fmaxf(a[u], dpp_xor1(a[u]));            // block max over the lane pair
+  }
+  uint32_t sbv[kNvUnroll], sb4v[FS ? kNvUnroll : 1];
+  float sv[kNvUnroll], rv[kNvUnroll], s4v[FS ? kNvUnroll : 1], r4v[FS ? kNvUnroll : 1];
+  auto scales_of = [&](float am, float div, uint32_t& sb, float& sc, float& rho) {
+    sb = 0;
+    if (am > 0.0f && st > 0.0f) sb = e4m3_ceil(am / div);
+    sc = st * e4m3_decode(sb);
+    rho = 1.0f / sc;
+  };
+  auto share = [&](uint32_t sb, float sc, float rho, uint32_t* sbo, float* so, float* ro, int u) {
+    const uint32_t sbp = (uint32_t)__float_as_int(dpp_xor1(__int_as_float((int)sb)));
+    const float sp = dpp_xor1(sc), rp = dpp_xor1(rho);
+    sbo[u] = odd ? sbp : sb;
+    so[u] = odd ? sp : sc;
+    ro[u] = odd ? rp : rho;
+    sbo[u + 1] = odd ? sb : sbp;
+    so[u + 1] = odd ? sc : sp;
+    ro[u + 1] = odd ? rho : rp;
+  };
+#pragma unroll
+  for (int u = 0; u < kNvUnroll; u += 2) {
+    const float am = odd ? a[u + 1] : a[u];
+    uint32_t sb;
+    float sc, rho;
+    scales_of(am, six_st, sb, sc, rho);
+    share(sb, sc, rho, sbv, sv, rv, u);
     if constexpr (FS) {
-      uint32_t sb4 = 0;
-      if (a > 0.0f && st > 0.0f) sb4 = e4m3_ceil(a / four_st);
-      const float s4 = st * e4m3_decode(sb4);
-      const float rho4 = 1.0f / s4;
-      const uint32_t p4 = (s4 == 0.0f) ? 0u : encode8_scaled(v[u], rho4);
+      scales_of(am, four_st, sb, sc, rho);
+      share(sb, sc, rho, sb4v, s4v, r4v, u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kNvUnroll; ++u) {
+    uint32_t sb = sbv[u];
+    const float s = sv[u];
+    uint32_t p = (s == 0.0f) ? 0u : encode8_scaled(v[u], rv[u]);
+    if constexpr (FS) {
+      const float s4 = s4v[u];
+      const uint32_t p4 = (s4 == 0.0f) ? 0u : encode8_scaled(v[u], r4v[u]);
       const float h6 = half_block_sq_error(v[u], p, s), h4 = half_block_sq_error(v[u], p4, s4);
       const float e6 = h6 + dpp_xor1(h6), e4 = h4 + dpp_xor1(h4);
       if (e4 < e6) {
-        sb = sb4;
+        sb = sb4v[u];
         p = p4;
       }
     }
