@@ -19,9 +19,11 @@ int device_cus();
 hipError_t launch_quant_nvfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, int ts_is_input,
                               int four_six, hipStream_t s);
-// Writes max|x| into the tensor-scale cell (amax encoding).  scratch (may be
-// NULL with scratch_bytes == 0) holds per-workgroup partial maxima when it
-// is large enough; its contents are destroyed.
+// Writes the tensor maximum A = max|x| into the tensor-scale cell: with one
+// workgroup as flag | A (amax encoding), after per-workgroup partial maxima
+// (in scratch, when it is large enough; may be NULL with scratch_bytes ==
+// 0; its contents are destroyed) as s_t = fl(A / 1536) itself.  The NVFP4
+// quantizer reads either form.
 hipError_t launch_amax_to_cell(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,
                                float* cell, uint8_t* scratch, int64_t scratch_bytes, hipStream_t s);
 hipError_t launch_quant_mxfp4(const void* x, int bf16, int64_t rows, int64_t cols, int64_t ldx,

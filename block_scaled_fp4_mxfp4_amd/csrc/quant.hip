@@ -176,7 +176,9 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
-    *cell = kAmaxFlag | m;
+    // s_t itself (flag clear): the quantization kernel's threads then read
+    // it instead of each dividing A by 1536
+    *cell = __float_as_uint(__uint_as_float(m) / 1536.0f);
   }
 }
 
