@@ -107,14 +107,26 @@ class ClockSampler:
         return out
 
 
+# --config names (the workloads of synth.py) -> what bench.py runs for them
+CONFIGS = {
+    "nvfp4_tiny": "tiny",
+    "nvfp4_prefill": None,                  # the headline step alone (--only-step)
+    "mxfp4_transform": "mxfp4",
+    "nvfp4_decode": "decode",
+    "looped_sigma_delta": "sigma_delta",
+}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", "--iters", dest="steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-extras", action="store_true")
-    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cpu-baseline", "--no-oracle", dest="no_cpu_baseline", action="store_true")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
+    p.add_argument("--config", default=None, choices=sorted(CONFIGS),
+                   help="one workload alone: the headline step (nvfp4_prefill) or one of the other rows")
     p.add_argument("--extras", default=None,
                    help="comma list of extras to run alone, without the headline step (for profiling): "
                         "mxfp4, macaq, nvfp4_46, harmonize, decode, sigma_delta, tiny")
@@ -126,7 +138,12 @@ def parse():
                    help="run only torch's copy, fill and sum on rotated buffers (practical HBM rates of this box)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (HBM byte-counter calibration)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.config == "nvfp4_prefill":
+        args.only_step = True
+    elif args.config is not None:
+        args.extras = CONFIGS[args.config]
+    return args
 
 
 def main():
