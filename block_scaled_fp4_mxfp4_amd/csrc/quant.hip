@@ -94,6 +94,24 @@ __device__ __forceinline__ int64_t chunk_offset(int64_t c, int64_t cpr, int64_t 
 // never stored (nor can it change a maximum).
 __device__ __forceinline__ int64_t clamp_chunk(int64_t c, int64_t n) { return c < n ? c : n - 1; }
 
+// Row and column (in chunks) of chunk base + loc, rows of cpr chunks, with
+// r0 = base / cpr and c0 = base % cpr computed once per workgroup (base is
+// uniform): for rows of at least `span` chunks (loc < span) the column
+// wraps at most once, so there is no per-thread division.
+__device__ __forceinline__ void chunk_row_col(int64_t r0, int64_t c0, int loc, int span, int64_t cpr,
+                                              int64_t& row, int64_t& col) {
+  col = c0 + loc;
+  row = r0;
+  if (cpr >= span) {
+    const bool wrap = col >= cpr;
+    col = wrap ? col - cpr : col;
+    row = wrap ? row + 1 : row;
+  } else {
+    row += col / cpr;
+    col = col % cpr;
+  }
+}
+
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- amax ----
@@ -350,12 +368,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(
     const float* __restrict__ t, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   float v[kMxUnroll][8], ts[SCALE ? kMxUnroll : 1][8];
   int64_t cidx[kMxUnroll];
+  const int64_t base = (int64_t)blockIdx.x * kMxUnroll * kThreads;
+  const int64_t r0 = SCALE ? base / cpr : 0, c0 = SCALE ? base - r0 * cpr : 0;   // uniform
 #pragma unroll
   for (int u = 0; u < kMxUnroll; ++u) {              // all loads first
-    cidx[u] = ((int64_t)blockIdx.x * kMxUnroll + u) * kThreads + threadIdx.x;
+    cidx[u] = base + u * kThreads + threadIdx.x;
     const int64_t cl = clamp_chunk(cidx[u], nchunks);
     load8<BF16>(x, chunk_offset<CONTIG>(cl, cpr, ld), v[u]);
-    if constexpr (SCALE) load8<false>(t, (cl % cpr) * 8, ts[u]);
+    if constexpr (SCALE) {
+      // the channel scales of chunk cidx's column (past the end: some
+      // in-range column; that chunk is not stored)
+      int64_t row, col;
+      chunk_row_col(r0, c0, u * kThreads + (int)threadIdx.x, kMxUnroll * kThreads, cpr, row, col);
+      load8<false>(t, col * 8, ts[u]);
+    }
   }
   const int qlane = threadIdx.x & 3;
 #pragma unroll
@@ -385,15 +411,18 @@ template <bool BF16, bool CONTIG, bool SCALE>
 __global__ __launch_bounds__(kThreads) void k_hadamard32(
     const void* __restrict__ x, int64_t nchunks, int64_t cpr, int64_t ld,
     const float* __restrict__ t, float* __restrict__ y, int64_t ldy) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kThreads;
+  const int64_t c = base + threadIdx.x;
   const int64_t cl = clamp_chunk(c, nchunks);
+  const int64_t r0 = base / cpr, c0 = base - r0 * cpr;                         // uniform
+  int64_t row, col;                                  // of chunk c
+  chunk_row_col(r0, c0, (int)threadIdx.x, kThreads, cpr, row, col);
   float v[8];
   load8<BF16>(x, chunk_offset<CONTIG>(cl, cpr, ld), v);
-  if constexpr (SCALE) apply_chan_scale(v, t, (cl % cpr) * 8);
+  if constexpr (SCALE) apply_chan_scale(v, t, col * 8);   // past the end: an in-range column, not stored
   hadamard32_lane(v, threadIdx.x & 3);
   if (c < nchunks) {
-    const int64_t r = c / cpr;
-    float4* p = reinterpret_cast<float4*>(y + r * ldy + (c - r * cpr) * 8);
+    float4* p = reinterpret_cast<float4*>(y + row * ldy + col * 8);
     p[0] = make_float4(v[0], v[1], v[2], v[3]);
     p[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
