@@ -301,18 +301,40 @@ __global__ __launch_bounds__(kThreads) void k_decode(
 // 16-block (DPP); put(r, c8, codes, scale) stores one chunk's four code
 // bytes and, on even c8, the block scale.  PAIRED: each lane of a pair
 // computes the block scales of one of two chunks and passes them to the
-// other (fewer instructions, more live registers).  Returns the tensor
-// scale.
+// other, and chunk rows and columns advance without a division per chunk
+// (fewer instructions, more live registers).  Returns the tensor scale.
 template <int NT, int U, bool PAIRED, typename Put>
 __device__ __forceinline__ float quantize_act_block(const uint16_t* __restrict__ A, int64_t lda, int M, int K,
                                                     float ats_in, bool dynamic, float* red, Put put) {
   const int tid = threadIdx.x, cpr = K / 8, nch = M * cpr;
+  // row and column of chunk tid + u NT: one division per thread, then
+  // steps of NT chunks (q_nt rows and r_nt < cpr columns: at most one wrap)
+  const int q_nt = NT / cpr, r_nt = NT - q_nt * cpr;      // uniform
+  const int row0 = tid / cpr, col0 = tid - row0 * cpr;
+  auto advance = [&](int& row, int& col) {
+    row += q_nt;
+    col += r_nt;
+    if (col >= cpr) {
+      col -= cpr;
+      ++row;
+    }
+  };
   uint4 q[U];
+  if constexpr (PAIRED) {
+    int row = row0, col = col0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = tid + u * NT;
-    const int cc = c < nch ? c : 0;                        // chunk 0 is real data: harmless to the max
-    q[u] = *reinterpret_cast<const uint4*>(A + (int64_t)(cc / cpr) * lda + (cc % cpr) * 8);
+    for (int u = 0; u < U; ++u) {
+      const bool in = tid + u * NT < nch;                  // else chunk 0, real data: harmless to the max
+      q[u] = *reinterpret_cast<const uint4*>(A + (in ? (int64_t)row * lda + col * 8 : 0));
+      advance(row, col);
+    }
+  } else {                                                 // fewer live registers: a division per chunk
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = tid + u * NT;
+      const int cc = c < nch ? c : 0;
+      q[u] = *reinterpret_cast<const uint4*>(A + (int64_t)(cc / cpr) * lda + (cc % cpr) * 8);
+    }
   }
   float ats = ats_in;
   if (dynamic) {
@@ -359,6 +381,8 @@ __device__ __forceinline__ float quantize_act_block(const uint16_t* __restrict__
     sc = ats * e4m3_decode(sb);
     rho = 1.0f / sc;
   };
+  // emits chunks in increasing u, walking the same rows and columns again
+  int erow = row0, ecol = col0;
   auto emit = [&](int u, const float v[8], uint32_t sb, float sc, float rho) {
     const int c = tid + u * NT;
     uint32_t p = 0;
@@ -366,7 +390,12 @@ __device__ __forceinline__ float quantize_act_block(const uint16_t* __restrict__
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2] * rho, v[3] * rho, 1.0f, 1);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4] * rho, v[5] * rho, 1.0f, 2);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6] * rho, v[7] * rho, 1.0f, 3);
-    if (c < nch) put(c / cpr, c % cpr, (sc == 0.0f) ? 0u : p, sb);
+    if constexpr (PAIRED) {
+      if (c < nch) put(erow, ecol, (sc == 0.0f) ? 0u : p, sb);
+      advance(erow, ecol);
+    } else {
+      if (c < nch) put(c / cpr, c % cpr, (sc == 0.0f) ? 0u : p, sb);
+    }
   };
   if constexpr (!PAIRED) {                                // fewer live registers: both lanes do all
 #pragma unroll
