@@ -46,6 +46,12 @@
                                 // at 2048 x 14336 x 4096); the W4A16 GEMMs are 6% faster with
                                 // non-temporal ones, like the NVFP4 step
 #endif
+#ifndef FP4Q_NV_SPREAD
+#define FP4Q_NV_SPREAD 6        // NVFP4 next-stage loads in 6 parts over the first 6 of 8 slices: 5.9%
+                                // faster at 4096 x 10240 x 5120 than all of them after the barrier
+                                // (349.5 against 371.6 us; 4, 5, 7, 8 parts: 356-362 us); MXFP4
+                                // gained nothing from spreading its loads
+#endif
 #ifndef FP4Q_NV_SCHED_SPLIT
 #define FP4Q_NV_SCHED_SPLIT 0   // 1: one scheduling region per 16-element block half
 #endif
@@ -293,26 +299,37 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
   }
 
   const uint32_t smem_base = lds_offset(smem);
-  auto issue = [&](int kt) {
+  // Issues this wavefront's loads of stage kt whose index in the list
+  // (A units, B units, A scale words, B scale words) is `part` modulo P;
+  // P = 1 issues them all.
+  auto issue = [&](int kt, int part = 0, int P = 1) {
     const uint32_t st = smem_base + (uint32_t)((kt % NS) * Lay::STAGE);
     const uint32_t kc = (uint32_t)kt * CB, ksc = (uint32_t)kt * Lay::SCB, kca = (uint32_t)kt * Lay::A_ROWB;
+    int idx = 0;
 #pragma unroll
-    for (int i = 0; i < Lay::A_LD; ++i)
-      if (i * NT + wave * 64 < Lay::A_N)                 // wave-uniform
+    for (int i = 0; i < Lay::A_LD; ++i, ++idx)
+      if (idx % P == part && i * NT + wave * 64 < Lay::A_N)       // wave-uniform
         dma16(p.A, offA[i] + kca, st + Lay::A_OFF + (i * NT + wave * 64) * 16);
 #pragma unroll
-    for (int i = 0; i < Lay::B_LD; ++i)
-      if (i * NT + wave * 64 < Lay::B_N)
+    for (int i = 0; i < Lay::B_LD; ++i, ++idx)
+      if (idx % P == part && i * NT + wave * 64 < Lay::B_N)
         dma16(p.B, offB[i] + kc, st + Lay::B_OFF + (i * NT + wave * 64) * 16);
 #pragma unroll
-    for (int i = 0; i < Lay::SA_LD; ++i)
-      if (i * NT + wave * 64 < Lay::SA_N)
+    for (int i = 0; i < Lay::SA_LD; ++i, ++idx)
+      if (idx % P == part && i * NT + wave * 64 < Lay::SA_N)
         dma4(p.As, offSA[i] + ksc, st + Lay::SA_OFF + (i * NT + wave * 64) * 4);
 #pragma unroll
-    for (int i = 0; i < Lay::SB_LD; ++i)
-      if (i * NT + wave * 64 < Lay::SB_N)
+    for (int i = 0; i < Lay::SB_LD; ++i, ++idx)
+      if (idx % P == part && i * NT + wave * 64 < Lay::SB_N)
         dma4(p.Bs, offSB[i] + ksc, st + Lay::SB_OFF + (i * NT + wave * 64) * 4);
   };
+  // NVFP4 on 32 x 32 instructions issues the next stage's loads in SPREAD
+  // parts, one at the start of each of the stage's first SPREAD slices
+  // (CB / 32 steps of four 16-K instructions), instead of all of them right
+  // after the barrier: every wavefront then waits less for the address
+  // unit to take its loads before it can go on with its own multiplies.
+  constexpr int SPREAD = (FMT == FMT_NV && M32) ? FP4Q_NV_SPREAD : 0;
+  static_assert(SPREAD <= CB / 32 * 4, "one part per slice at most");
   // loads this wavefront issues per stage (wave-uniform)
   int nload = 0;
 #pragma unroll
@@ -345,7 +362,9 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
     wait_vm(ahead * nload);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    const bool more = kt + NS - 1 < KT;                // a stage is left to load
+    if constexpr (SPREAD == 0)
+      if (more) issue(kt + NS - 1);
     if constexpr (FMT == FMT_MX && M32) {
       // Step ks covers K elements [64 ks, 64 ks + 64) of the stage; lane half
       // hh reads 16-byte chunk 2 ks + hh of its row: one 32-element MXFP4
@@ -496,6 +515,8 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (ks | t) __builtin_amdgcn_sched_barrier(0);
+          if constexpr (SPREAD > 0)
+            if (ks * 4 + t < SPREAD && more) issue(kt + NS - 1, ks * 4 + t, SPREAD);
           v8h ha[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
