@@ -52,6 +52,11 @@
                                 // (349.5 against 371.6 us; 4, 5, 7, 8 parts: 356-362 us); MXFP4
                                 // gained nothing from spreading its loads
 #endif
+#ifndef FP4Q_W16_SPREAD
+#define FP4Q_W16_SPREAD 3       // W4A16 the same over 3 of its 4 slices: the looped core's 13 GEMMs 7.4%
+                                // faster grouped (187.8 against 202.8 us), 6.4% as single launches
+                                // (2 or 4 parts: 190.8-190.9 us grouped)
+#endif
 #ifndef FP4Q_NV_SCHED_SPLIT
 #define FP4Q_NV_SCHED_SPLIT 0   // 1: one scheduling region per 16-element block half
 #endif
@@ -323,13 +328,14 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
       if (idx % P == part && i * NT + wave * 64 < Lay::SB_N)
         dma4(p.Bs, offSB[i] + ksc, st + Lay::SB_OFF + (i * NT + wave * 64) * 4);
   };
-  // NVFP4 on 32 x 32 instructions issues the next stage's loads in SPREAD
-  // parts, one at the start of each of the stage's first SPREAD slices
-  // (CB / 32 steps of four 16-K instructions), instead of all of them right
-  // after the barrier: every wavefront then waits less for the address
-  // unit to take its loads before it can go on with its own multiplies.
-  constexpr int SPREAD = (FMT == FMT_NV && M32) ? FP4Q_NV_SPREAD : 0;
-  static_assert(SPREAD <= CB / 32 * 4, "one part per slice at most");
+  // NVFP4 on 32 x 32 instructions and W4A16 issue the next stage's loads
+  // in SPREAD parts, one at the start of each of the stage's first SPREAD
+  // slices (NVFP4: CB / 32 steps of four 16-K instructions; W4A16: 8-element
+  // slices of the two block halves), instead of all of them right after the
+  // barrier: every wavefront then waits less for the address unit to take
+  // its loads before it can go on with its own multiplies.
+  constexpr int SPREAD = (FMT == FMT_NV && M32) ? FP4Q_NV_SPREAD : FMT == FMT_W16 ? FP4Q_W16_SPREAD : 0;
+  static_assert(SPREAD <= (M32 ? CB / 32 * 4 : KS * 4), "one part per slice at most");
   // loads this wavefront issues per stage (wave-uniform)
   int nload = 0;
 #pragma unroll
@@ -460,6 +466,8 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
           }
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
+            if constexpr (SPREAD > 0)
+              if ((ks * 2 + h) * 2 + s2 < SPREAD && more) issue(kt + NS - 1, (ks * 2 + h) * 2 + s2, SPREAD);
             v8bf ha[FM];
             const int ch = 16 * ks + 4 * g + 2 * h + s2;     // bf16 chunk within the staged row
 #pragma unroll
