@@ -444,6 +444,17 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j & 1], acc[i][j], 4, 4, 0, fsa[i],
                                                                          0, fsb[j & 1]);
         }
+        // Scheduling groups that keep the reads of B block j + 1 (codes
+        // and scale byte) ahead of block j's multiplies.  Left alone, the
+        // scheduler issued each read after the multiplies of the block
+        // before, into the same registers, and every block then waited
+        // for its read (the groups: 1.9-3.6% faster, bit-identical).
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + 2, 0);          // A blocks, B block 0
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (j + 1 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // B block j + 1
+          __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                // block j's multiplies
+        }
       }
     } else if constexpr (FMT == FMT_W16) {
       // bf16 A x NVFP4 B: the same K assignment as the NVFP4 path (lane
