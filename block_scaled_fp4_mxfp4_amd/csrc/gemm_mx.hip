@@ -509,16 +509,22 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
 #pragma unroll
       for (int ks = 0; ks < CB / 32; ++ks) {
         const int c = 2 * ks + hh;
+        // scale pairs first, then codes: the scale conversions then wait
+        // only for the small reads, not for every code read behind them
+        // (reads interleaved per block: 3.4% slower at 4096 x 10240 x 5120)
+        uint32_t ra[FM], rb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          ra[i] = *reinterpret_cast<const uint16_t*>(st + Lay::SA_OFF + (wm * RW + i * 32 + r32) * Lay::SCB + 2 * c);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          rb[j] = *reinterpret_cast<const uint16_t*>(st + Lay::SB_OFF + (wn * (BN / 2) + j * 32 + r32) * Lay::SCB + 2 * c);
         uint4 qa[FM];
         v2h sa[FM][2];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int row = wm * RW + i * 32 + r32;
           qa[i] = *reinterpret_cast<const uint4*>(st + Lay::A_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
-          const uint32_t b2 = *reinterpret_cast<const uint16_t*>(st + Lay::SA_OFF + row * Lay::SCB + 2 * c);
-          const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 1.0f, false));
-          sa[i][0] = v2h{t[0], t[0]};
-          sa[i][1] = v2h{t[1], t[1]};
         }
         uint4 qb[FN];
         v2h sb[FN][2];
@@ -526,8 +532,16 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
         for (int j = 0; j < FN; ++j) {
           const int row = wn * (BN / 2) + j * 32 + r32;
           qb[j] = *reinterpret_cast<const uint4*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
-          const uint32_t b2 = *reinterpret_cast<const uint16_t*>(st + Lay::SB_OFF + row * Lay::SCB + 2 * c);
-          const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 1.0f, false));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ra[i], 1.0f, false));
+          sa[i][0] = v2h{t[0], t[0]};
+          sa[i][1] = v2h{t[1], t[1]};
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const v2h t = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rb[j], 1.0f, false));
           sb[j][0] = v2h{t[0], t[0]};
           sb[j][1] = v2h{t[1], t[1]};
         }
