@@ -406,6 +406,15 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j & 1], acc[i][j], 4, 4, 0, fsa[i],
                                                                         0, fsb[j & 1]);
         }
+        // the same scheduling groups as the 16 x 16 path below (without
+        // them this path was 3-8% slower than that one; with them 3-5%
+        // faster on the same tiles)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + 2, 0);          // A blocks, B block 0
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (j + 1 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // B block j + 1
+          __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                // block j's multiplies
+        }
       }
     } else if constexpr (FMT == FMT_MX) {
       // Instruction step ks covers K elements [128 ks, 128 ks + 128) of the
@@ -738,9 +747,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_mx3_grouped(const MxGrou
 }
 
 #ifndef FP4Q_MX_M32
-#define FP4Q_MX_M32 0         // 1: 32 x 32 x 64 FP4 instructions (bit-exact too, but 5-8% slower on the
-                              // 2048 x 14336 x 4096 GEMM at every tile and ring tried: its loop is
-                              // not bound by the instruction rate)
+#define FP4Q_MX_M32 1         // 256-wide tiles on 32 x 32 x 64 FP4 instructions: 4.8% faster than
+                              // 16 x 16 x 128 at 2048 x 16384 x 4096 (92.8 against 97.5 us); the
+                              // 224-wide tiles (2048 x 14336) stay on 16 x 16, which 224 / 2 needs
 #endif
 #ifndef FP4Q_MX_BN
 #define FP4Q_MX_BN 256        // workgroup columns (16 x 16 path: 224 for widths that 224 divides and 256 does not)
@@ -826,12 +835,12 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
   // grows with its width, so the width with the smaller rounds x width
   // wins (ties: 256).  For 2048 x 14336: 256 -> 448 tiles, 2 rounds x 256;
   // 224 -> 512 tiles, 2 rounds x 224 (measured 5% faster).
-  if constexpr (FP4Q_MX_BN == 256 && FP4Q_MX_CB == 128 && !FP4Q_MX_M32) {
+  if constexpr (FP4Q_MX_BN == 256 && FP4Q_MX_CB == 128) {
     const int64_t cus = device_cus(), tm = cdiv_i(M, FP4Q_MX_BM);
     const int64_t c256 = cdiv_i(tm * cdiv_i(N, 256), cus) * 256;
     const int64_t c224 = cdiv_i(tm * cdiv_i(N, 224), cus) * 224;
     if (c224 < c256)
-      return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS>(p, s);
+      return launch_mx3<FMT_MX, FP4Q_MX_BM, 224, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS, 0>(p, s);
   }
   return launch_mx3<FMT_MX, FP4Q_MX_BM, FP4Q_MX_BN, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS, FP4Q_MX_M32>(p, s);
 }
