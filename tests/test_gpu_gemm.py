@@ -103,8 +103,9 @@ def test_mxfp4_gemm_small_ragged(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(2048, 8192, 256), (200, 300, 512)])
 def test_mxfp4_gemm_both_column_tiles(M, N, K):
     # the launcher picks the column tile by rounds over the compute units:
-    # 2048 x 8192 fills one round with 256-wide tiles (224 would need two);
-    # 200 x 300 takes 224-wide tiles, ragged in both M and N
+    # 2048 x 8192 fills one round with 256-wide tiles (224 would need two),
+    # which run on 32 x 32 x 64 instructions; 200 x 300 takes 224-wide tiles
+    # on 16 x 16 x 128, ragged in both M and N
     x = synth.heavy_tailed_f32(220 + M, 221, (M, K))
     w = synth.normal_f32(222 + N, (N, K), 0.02)
     L = fp4q()
