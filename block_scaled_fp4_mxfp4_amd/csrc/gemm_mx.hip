@@ -1,20 +1,24 @@
 // gemm_mx.hip -- MXFP4 W4A4 prefill GEMM on gfx950's block-scaled FP4
 // matrix cores ("MACaQ", core method: y = [(x*t)B]_MXFP4 W'^T_MXFP4).
 //
-// Each v_mfma_scale_f32_16x16x128_f8f6f4 consumes, per lane, 32 packed E2M1
-// codes of one row and the E8M0 byte of exactly that 32-element block, so
-// the OCP MXFP4 tensors feed the instruction as stored: no dequantization.
+// Each v_mfma_scale_f32_16x16x128_f8f6f4 (and its 32 x 32 x 64 form)
+// consumes, per lane, 32 packed E2M1 codes of one row and the E8M0 byte of
+// exactly that 32-element block, so the OCP MXFP4 tensors feed the
+// instruction as stored: no dequantization.  The same template runs the
+// exact-NVFP4 GEMM (fp16 matrix instructions after an exact dequantization)
+// and the W4A16 GEMM (bf16).
 //
 // Data movement (the part that decides speed here):
-//  * a 512-thread workgroup owns a BM x BN tile (256 x 224 or 256 x 256);
-//    its eight wavefronts (two per SIMD, so one wave's dequantization or
-//    LDS reads overlap the other's matrix instructions) own 64 x BN/2 each,
-//    i.e. 4 x (BN/32) 16 x 16 accumulator tiles;
+//  * a 512-thread workgroup owns a BM x BN tile (MXFP4: 256 x 224 on
+//    16 x 16 instructions, or 256 x 256 on 32 x 32); its eight wavefronts
+//    (two per SIMD, so one wave's dequantization or LDS reads overlap the
+//    other's matrix instructions) own 64 x BN/2 each;
 //  * K advances 256 elements (one whole 128-byte line of codes per row) per
 //    stage through a two-slot LDS ring filled by direct global->LDS loads
 //    (global_load_lds, 16 bytes per lane) issued one stage ahead, so no
 //    registers are spent on staging and the loads of stage k + 1 overlap
-//    the 2 x 8 x (BN/32) matrix instructions of stage k;
+//    the matrix instructions of stage k (the NVFP4 and W4A16 forms issue
+//    them in parts over the stage's first slices);
 //  * a row's eight 16-byte chunks are stored XOR-swizzled by
 //    (row ^ ((row >> 3) & 1)) & 7, which puts the 16-byte fragment reads of
 //    16 consecutive rows on disjoint banks whether the LDS serves 128 or
