@@ -100,6 +100,20 @@ __device__ __forceinline__ v8bf dequant8_bf16(uint32_t w, float sb) {
   return __builtin_bit_cast(v8bf, uint4{o[0], o[1], o[2], o[3]});
 }
 
+// Dword q (values 2q, 2q + 1) of dequant8_bf16, the same operations.
+__device__ __forceinline__ uint32_t dequant2_bf16(uint32_t w, float sb, int q) {
+  float lo, hi;
+  switch (q) {
+    case 0: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); lo = p[0]; hi = p[1]; break; }
+    case 1: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); lo = p[0]; hi = p[1]; break; }
+    case 2: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); lo = p[0]; hi = p[1]; break; }
+    default: { auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); lo = p[0]; hi = p[1]; break; }
+  }
+  lo = lo * sb;
+  hi = hi * sb;
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // E4M3 block scale (non-negative byte) -> the same value in fp16 (every
 // E4M3 value, subnormals included, is an fp16 normal), splatted to both
 // halves; one hardware fp8 -> fp16 convert.
@@ -244,7 +258,7 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
   constexpr int WM = NW / 2, RW = BM / WM;        // wavefront rows, rows per wavefront
   static_assert(BM % 64 == 0 && BM <= 512 && BN % 32 == 0 && BN <= 320 && (CB == 64 || CB == 128), "tile");
   static_assert((NW == 4 || NW == 8) && NS >= 2 && NS <= 4 && RW % 16 == 0, "layout");
-  static_assert(!M32 || (RW % 32 == 0 && (BN / 2) % 32 == 0 && FMT != FMT_W16), "32 x 32 tiles");
+  static_assert(!M32 || (RW % 32 == 0 && (BN / 2) % 32 == 0), "32 x 32 tiles");
   constexpr int TS = M32 ? 32 : 16;               // accumulator tile edge
   constexpr int FM = RW / TS, FN = BN / (2 * TS);
   using Acc = typename std::conditional<M32 != 0, v16f, v4f>::type;
@@ -467,6 +481,77 @@ __device__ __forceinline__ void mx3_tile(const MxArgs& p, int bid) {
         for (int j = 0; j < FN; ++j) {
           if (j + 1 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // B block j + 1
           __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                // block j's multiplies
+        }
+      }
+    } else if constexpr (FMT == FMT_W16 && M32) {
+      // bf16 A x NVFP4 B on 32 x 32 x 16 bf16 instructions, with the K
+      // assignment of the NVFP4 32 x 32 path: step ks, lane half hh -> B
+      // chunk c = 2 ks + hh, its dword t -> instruction t; the matching 8 bf16
+      // values of A are its staged 16-byte chunk 8 ks + 4 hh + t
+      const uint8_t* st = smem + (kt % NS) * Lay::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < CB / 32; ++ks) {
+        const int c = 2 * ks + hh;
+        uint32_t rb[FN];                               // scale pairs first, as in the NVFP4 path
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          rb[j] = *reinterpret_cast<const uint16_t*>(st + Lay::SB_OFF + (wn * (BN / 2) + j * 32 + r32) * Lay::SCB + 2 * c);
+        uint4 qb[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * (BN / 2) + j * 32 + r32;
+          qb[j] = *reinterpret_cast<const uint4*>(st + Lay::B_OFF + row * CB + ((c ^ swz<CB>(row)) << 4));
+        }
+        float sbf[FN][2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const auto sp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rb[j], 1.0f, false);
+          sbf[j][0] = sp[0];
+          sbf[j][1] = sp[1];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (ks | t) __builtin_amdgcn_sched_barrier(0);
+          if constexpr (SPREAD > 0)
+            if (ks * 4 + t < SPREAD && more) issue(kt + NS - 1, ks * 4 + t, SPREAD);
+          v8bf ha[FM];
+          const int ch = 8 * ks + 4 * hh + t;          // bf16 chunk within the staged row
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * RW + i * 32 + r32;
+            ha[i] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF + row * Lay::A_ROWB + ((ch ^ (row & 15)) << 4));
+          }
+          __builtin_amdgcn_s_setprio(1);
+          // B block j + 1 dequantized in FM parts behind block j's multiplies,
+          // into the other of two register sets
+          uint32_t hb[2][4];
+          {
+            const uint32_t w = t == 0 ? qb[0].x : t == 1 ? qb[0].y : t == 2 ? qb[0].z : qb[0].w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hb[0][q] = dequant2_bf16(w, sbf[0][t >> 1], q);
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const v8bf cur = __builtin_bit_cast(v8bf, uint4{hb[j & 1][0], hb[j & 1][1], hb[j & 1][2], hb[j & 1][3]});
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[i], cur, acc[i][j], 0, 0, 0);
+              if (j + 1 < FN) {
+                const int jn = j + 1 < FN ? j + 1 : j;
+                const uint32_t w = t == 0 ? qb[jn].x : t == 1 ? qb[jn].y : t == 2 ? qb[jn].z : qb[jn].w;
+#pragma unroll
+                for (int q = i * 4 / FM; q < (i + 1) * 4 / FM; ++q) hb[(j + 1) & 1][q] = dequant2_bf16(w, sbf[jn][t >> 1], q);
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one matrix instruction
+              if (j + 1 < FN) __builtin_amdgcn_sched_group_barrier(0x002, 16 / FM, 0);  // then VALU
+            }
+          __builtin_amdgcn_s_setprio(0);
         }
       }
     } else if constexpr (FMT == FMT_W16) {
@@ -849,11 +934,23 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, const uint8_t*
   return launch_mx3<FMT_MX, FP4Q_MX_BM, FP4Q_MX_BN, FP4Q_MX_CB, FP4Q_MX_MINB, FP4Q_MX_NW, FP4Q_MX_NS, FP4Q_MX_M32>(p, s);
 }
 
+// W4A16 runs on 32 x 32 x 16 bf16 instructions (the 16 x 16 x 32 shape
+// sustains about half their rate): the looped core's 13 GEMMs 4% faster
+// grouped (187.1 against 194.8 us) and 3% as single launches (256.7
+// against 264.0 us, 256 x 64 tiles; 128 x 128: 281.3, 128 x 64: 267.7).
+// Both forms keep the same K order per output, so a grouped launch equals
+// single launches bit for bit.
+#ifndef FP4Q_W16G_M32
+#define FP4Q_W16G_M32 1
+#endif
+#ifndef FP4Q_W16M_M32
+#define FP4Q_W16M_M32 1
+#endif
 #ifndef FP4Q_W16M_BM
-#define FP4Q_W16M_BM 128      // small tiles: the looped core has N, K in {768, 3072} (measured)
+#define FP4Q_W16M_BM 256      // single launches (16 x 16 form: 128 x 96 was the best of 64, 96, 128 wide)
 #endif
 #ifndef FP4Q_W16M_BN
-#define FP4Q_W16M_BN 96       // 768-wide outputs: 8 x 32 = 256 tiles at M = 4096 (measured best of 64, 96, 128)
+#define FP4Q_W16M_BN 64
 #endif
 #ifndef FP4Q_W16M_CB
 #define FP4Q_W16M_CB 64
@@ -877,7 +974,7 @@ hipError_t launch_gemm_w4a16_direct(const void* a, int64_t lda, const uint8_t* b
                                     const float* bts, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
                                     hipStream_t s) {
   MxArgs p{reinterpret_cast<const uint8_t*>(a), nullptr, b, bs, nullptr, bts, M, N, K, y, ldy, 0, 0, lda};
-  return launch_mx3<FMT_W16, FP4Q_W16M_BM, FP4Q_W16M_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2>(p, s);
+  return launch_mx3<FMT_W16, FP4Q_W16M_BM, FP4Q_W16M_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2, FP4Q_W16M_M32>(p, s);
 }
 
 hipError_t launch_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, hipStream_t s) {
@@ -912,7 +1009,7 @@ hipError_t launch_gemm_w4a16_grouped(const fp4q_w4a16_problem* probs, int n, hip
       wg += a.tiles_m * a.tiles_n;
     }
     g.start[g.n] = wg;
-    hipLaunchKernelGGL((k_gemm_mx3_grouped<FMT_W16, FP4Q_W16G_BM, FP4Q_W16G_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2, 0>),
+    hipLaunchKernelGGL((k_gemm_mx3_grouped<FMT_W16, FP4Q_W16G_BM, FP4Q_W16G_BN, FP4Q_W16M_CB, 1, FP4Q_W16M_NW, 2, FP4Q_W16G_M32>),
                        dim3((unsigned)wg), dim3(FP4Q_W16M_NW * 64), 0, s, g);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
