@@ -57,9 +57,10 @@
                                 // gained nothing from spreading its loads
 #endif
 #ifndef FP4Q_W16_SPREAD
-#define FP4Q_W16_SPREAD 3       // W4A16 the same over 3 of its 4 slices: the looped core's 13 GEMMs 7.4%
-                                // faster grouped (187.8 against 202.8 us), 6.4% as single launches
-                                // (2 or 4 parts: 190.8-190.9 us grouped)
+#define FP4Q_W16_SPREAD 6       // W4A16 (32 x 32 form, 8 slices) the same over 6 slices: the looped core's
+                                // 13 GEMMs 4.5% faster grouped than with 3 parts (179.4 against 187.8 us;
+                                // 2, 4, 7, 8 parts: 187.1, 183.0, 180.7, 184.1), 4% as single launches;
+                                // the 16 x 16 form gained 7.4% from 3 parts over its 4 slices
 #endif
 #ifndef FP4Q_NV_SCHED_SPLIT
 #define FP4Q_NV_SCHED_SPLIT 0   // 1: one scheduling region per 16-element block half
