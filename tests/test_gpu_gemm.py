@@ -118,11 +118,14 @@ def test_mxfp4_gemm_both_column_tiles(M, N, K):
     _check(y[np.ix_(rows, cols)], OG.w4a4_mxfp4(cx, sx, cw, sw), f"mxfp4 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(768, 22400, 128), (600, 25000, 384), (1000, 30000, 256), (300, 9000, 1152)])
+@pytest.mark.parametrize("M,N,K", [(768, 22400, 128), (600, 25000, 384), (1000, 30000, 256), (300, 9000, 1152),
+                                   (1000, 30000, 1024)])
 def test_mxfp4_gemm_many_tiles_ragged(M, N, K):
     # more output tiles than compute units, partial tiles in M and N, and K
-    # that is (1000 x 30000 x 256) or is not (K = 128, 384, 1152) a whole
-    # number of the direct-load kernel's 256-element stages
+    # that is (1000 x 30000 x 256 and x 1024) or is not (K = 128, 384, 1152)
+    # a whole number of the direct-load kernel's 256-element stages; the
+    # 1000 x 30000 shapes take 256-wide tiles, with one stage (K = 256) and
+    # with four (K = 1024)
     x = synth.heavy_tailed_f32(230 + M, 231, (M, K))
     w = synth.normal_f32(232 + K, (N, K), 0.02)
     L = fp4q()
